@@ -1,0 +1,14 @@
+"""MI355X-native routed MoE FFN layer: HIP kernels behind a small C ABI.
+
+`sparse_mixture_experts_moe_amd.binding` is the ctypes binding of the C ABI
+(same entry-point names as include/moe.h).  It is imported lazily so that the
+pure-host helpers (e.g. `costmodel`) work without the built library.
+"""
+__all__ = ["binding", "costmodel"]
+
+
+def __getattr__(name):
+    if name == "binding":
+        from . import binding
+        return binding
+    raise AttributeError(name)
