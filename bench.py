@@ -1,0 +1,208 @@
+"""Benchmark of the routed MoE FFN layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one call of moe_layer (router -> top-k softmax -> permutation ->
+grouped gate/up+activation -> grouped down projection -> combine with the
+shared branch) over one batch of synthetic tokens whose inputs are already in
+HBM.  Prints one JSON line: whole-job tokens/s, the dominant kernel's roofline
+fraction (algorithmic bytes or FLOP per launch over its average event-timed
+duration) and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+DEFAULT_WORKLOAD = "qwen_decode"
+METRIC = "MoE-layer tokens/s; grouped-GEMM MFMA % of peak (prefill), HBM % (decode)"
+KERNEL_SOURCES = ["ffn_stream.hip", "ffn_tiled.hip"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "sparse_mixture_experts_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--policy", default="auto", choices=["auto", "stream", "lds"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=0)
+    return ap.parse_args()
+
+
+def cpu_baseline(wl, n_tokens: int):
+    """Time the oracle (as it stands) on the first n_tokens tokens of the batch:
+    routing of those tokens, every expert they touch, the shared branch and
+    the combine, with expert weights decoded from their stored format inside
+    the timed region.  Host copies of the raw inputs are made beforehand."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle.formats import decode
+    from oracle.moe import layer
+    from workloads import host_expert, host_shared, to_bits
+
+    c = wl.cfg
+    xb = to_bits(wl.x[:n_tokens])
+    wrb = to_bits(wl.wr)
+    # routing of the sample decides which experts the oracle needs
+    x64 = decode(xb, c.act_dtype)
+    wr64 = decode(wrb, c.act_dtype)
+    from oracle.moe import router_logits, topk_softmax
+    idx, _ = topk_softmax(router_logits(x64, wr64), c.k)
+    used = sorted(set(int(e) for e in idx.reshape(-1)))
+    raw = {e: host_expert(wl, e) for e in used}
+    sh = host_shared(wl)
+
+    def expert(e):
+        w13, s13, w2, s2 = raw[e]
+        return decode(w13, c.w_dtype), s13, decode(w2, c.w_dtype), s2
+
+    t0 = time.perf_counter()
+    x = decode(xb, c.act_dtype)
+    wr = decode(wrb, c.act_dtype)
+    shared = None
+    if sh is not None:
+        shared = (decode(sh[0], c.shared_w_dtype), sh[1], decode(sh[2], c.shared_w_dtype), sh[3])
+    layer(x, wr, c.k, expert, shared, c.act, c.act_shared)
+    dt = time.perf_counter() - t0
+    threads = 1
+    for info in threadpool_info():
+        if info.get("user_api") == "blas":
+            threads = max(threads, int(info.get("num_threads", 1)))
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"float64 NumPy oracle, whole layer on the first {n_tokens} of {c.T} tokens "
+                       f"({len(used)} experts decoded from {c.w_dtype}), {dt:.1f} s")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_mixture_experts_moe_amd import binding as B
+    from sparse_mixture_experts_moe_amd import costmodel as cm
+    from workloads import CONFIGS, generate
+
+    B.lib()  # fails loudly if the HIP library is not built
+    cfg = CONFIGS[args.workload]
+    torch.cuda.set_device(0)
+    wl = generate(cfg, seed=0, weight_device="cuda")
+    wl.x, wl.wr = wl.x.cuda(), wl.wr.cuda()
+    p = B.make_problem(cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.act, cfg.act_shared,
+                       cfg.act_dtype, cfg.w_dtype, cfg.shared_w_dtype, args.policy)
+    ws_bytes = B.moe_layer_workspace_size(p)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    y = torch.empty((cfg.T, cfg.D), dtype=wl.x.dtype, device="cuda")
+    counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    kw = dict(x=wl.x, w_router=wl.wr, w13=wl.w13, s13=wl.s13, w2=wl.w2, s2=wl.s2,
+              w13_shared=wl.w13s, s13_shared=wl.s13s, w2_shared=wl.w2s, s2_shared=wl.s2s, y=y)
+    step_args = B.layer_args(**kw)
+    probe_args = B.layer_args(counts_out=counts, **kw)
+    stream = torch.cuda.current_stream()
+
+    B.moe_layer(p, probe_args, ws, ws_bytes, stream)
+    torch.cuda.synchronize()
+    touched = int((counts.cpu().numpy() > 0).sum())
+
+    for _ in range(args.warmup):
+        B.moe_layer(p, step_args, ws, ws_bytes, stream)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-stage HIP events recorded on the layer's stream
+    B.moe_timing_read()
+    B.moe_timing_enable(True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        B.moe_layer(p, step_args, ws, ws_bytes, stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    B.moe_timing_enable(False)
+    stages = B.moe_timing_read()
+    total_ms = t0.elapsed_time(t1)
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = cfg.T * args.steps / (total_ms / 1e3)
+
+    # dominant kernel and its roofline
+    name, (st_ms, st_n) = max(stages.items(), key=lambda kv: kv[1][0])
+    avg_ms = st_ms / max(st_n, 1)
+    launches_per_step = st_n / args.steps
+    per_launch = {
+        "ffn1_gate_up_act": (cm.gemm1_bytes(cfg, touched), cm.gemm1_flops(cfg)),
+        "ffn2_down": (cm.gemm2_bytes(cfg, touched), cm.gemm2_flops(cfg)),
+    }
+    bytes_, flops = per_launch.get(name, (0.0, 0.0))
+    bytes_ /= launches_per_step
+    flops /= launches_per_step
+    ai = flops / bytes_ if bytes_ else 0.0
+    wdt = "bf16" if cfg.act_dtype == "bf16" else "f32"
+    ridge = cm.PEAK_TFLOPS[wdt] * 1e12 / (cm.PEAK_HBM_GBS * 1e9)
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{name}_{cfg.name}.json")
+    if os.path.exists(tpath):
+        tj = json.load(open(tpath))
+        if tj.get("kernel_hash") == kernel_hash():
+            traffic = tj.get("bytes_per_launch")
+    if ai < ridge:
+        roof = {"bound": "hbm", "achieved": bytes_ / (avg_ms * 1e-3) / 1e9, "peak": cm.PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / (avg_ms * 1e-3) / 1e12,
+                "peak": cm.PEAK_TFLOPS[wdt], "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof.update({"kernel": name, "avg_launch_ms": avg_ms, "algorithmic_bytes": bytes_,
+                 "algorithmic_flops": flops})
+
+    gemm_ms = sum(stages[s][0] for s in ("ffn1_gate_up_act", "ffn2_down")) / args.steps
+    out = {
+        "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.act_dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "D": cfg.D, "E": cfg.E, "k": cfg.k,
+                   "I": cfg.I, "I_shared": cfg.I_shared, "act": cfg.act,
+                   "w_dtype": cfg.w_dtype, "touched_experts": touched, "policy": args.policy},
+        "roofline": roof,
+        "grouped_gemm": {
+            "ms_per_step": gemm_ms,
+            "mfma_frac_bf16": cm.gemm_flops(cfg) / (gemm_ms * 1e-3) / (cm.PEAK_TFLOPS["bf16"] * 1e12),
+            "hbm_frac_layer_bytes": cm.layer_bytes(cfg, touched) / (ms_per_step * 1e-3)
+            / (cm.PEAK_HBM_GBS * 1e9)},
+        "stages_ms_per_step": {k: v[0] / args.steps for k, v in stages.items()},
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample_tokens or {"qwen_decode": 8, "ling_decode": 16}.get(cfg.name, 16)
+        out["cpu_baseline"] = cpu_baseline(wl, min(n, cfg.T))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

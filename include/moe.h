@@ -1,0 +1,231 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed Mixture-of-Experts FFN layer.
+ *
+ * The layer is  y = Router(x) + SharedExpert(x)  ("Qwen 3.5 MoE on Ironwood"
+ * page, model-architecture section): fp32 router logits, top-k softmax with
+ * renormalisation, a stable permutation of the (token, slot) assignments by
+ * expert, a grouped gated expert FFN (gate/up projection fused with SwiGLU or
+ * tanh-GEGLU, then the down projection), and a routing-weighted combine plus an
+ * always-on shared expert or parallel dense MLP.  The op split follows the
+ * "CANN Qwen3-MoE" page (GMM enablement and routing optimisation: fused top-k
+ * softmax, init routing + expert token counts, grouped matmul, finalize routing).
+ *
+ * Conventions for every entry point
+ *  - Tensor pointers are DEVICE pointers to row-major, contiguous storage,
+ *    16-byte aligned.  Scalars and structs are host memory.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *    enqueues work on it and returns; nothing is copied device->host and no
+ *    call synchronises.  Device-side faults surface at the caller's next sync.
+ *  - The caller owns every buffer.  The library never allocates or frees
+ *    device memory and keeps no per-call state, so calls on different streams
+ *    are independent as long as their output and workspace buffers are
+ *    disjoint.
+ *  - Errors are return values (moe_status_t).  Nothing throws, aborts or
+ *    prints.  Validation is synchronous and happens before anything is
+ *    enqueued; a failed launch returns MOE_ERR_LAUNCH.
+ *  - Weight layout is [out, in]: W13[e] is [2I, D] with rows [0,I) the gate
+ *    projection and rows [I,2I) the up projection (the concatenated w13 of the
+ *    CANN Qwen3-MoE page, whose swiglu applies SiLU to the first half of the
+ *    chunked product); W2[e] is [D, I].  fp8 weights carry fp32 per-output-
+ *    channel scales s13[e][2I] and s2[e][D], applied after the reduction
+ *    ("Ling-2.6-1T with SGLang-JAX" page, section 5, per-channel scaling).
+ *  - Supported dtype combinations: {act F32, weights F32} and
+ *    {act BF16, weights BF16 or FP8_E4M3FN}; anything else is
+ *    MOE_ERR_UNSUPPORTED (no silent fallback).
+ *  - Limits: 1 <= k <= min(E, 32); E <= 1024; D, I, I_shared multiples of 64;
+ *    T*k and T*max(D, I) below 2^31.  T == 0 is valid and enqueues nothing.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* dtypes */
+#define MOE_F32         0
+#define MOE_BF16        1
+#define MOE_FP8_E4M3FN  2   /* OCP e4m3fn: bias 7, max 448, no inf, 0x7F/0xFF NaN */
+
+/* gated activations of the expert FFN */
+#define MOE_ACT_SILU       0   /* SwiGLU: SiLU(gate) * up            */
+#define MOE_ACT_GELU_TANH  1   /* GEGLU:  tanh-GELU(gate) * up       */
+
+/* tile policies of the grouped FFN */
+#define MOE_TILE_AUTO     0    /* chosen on the host from T*k/E            */
+#define MOE_TILE_STREAM   1    /* register-streamed weights, small groups  */
+#define MOE_TILE_LDS      2    /* LDS-tiled MFMA GEMM, large groups         */
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,          /* a required pointer is NULL               */
+  MOE_ERR_SHAPE = 2,         /* a size is out of the supported range     */
+  MOE_ERR_DTYPE = 3,         /* an unknown dtype / activation code       */
+  MOE_ERR_UNSUPPORTED = 4,   /* a valid but unsupported combination      */
+  MOE_ERR_WORKSPACE = 5,     /* workspace smaller than required          */
+  MOE_ERR_LAUNCH = 6         /* a kernel launch or HIP runtime call failed */
+} moe_status_t;
+
+/* Problem description (host struct, plain int32 fields). */
+typedef struct moe_problem {
+  int32_t T;              /* tokens                                          */
+  int32_t D;              /* hidden size                                     */
+  int32_t E;              /* routed experts                                  */
+  int32_t k;              /* experts per token                               */
+  int32_t I;              /* routed expert intermediate size                 */
+  int32_t I_shared;       /* shared expert / dense MLP intermediate, 0 = none */
+  int32_t act;            /* MOE_ACT_* of the routed experts                 */
+  int32_t act_shared;     /* MOE_ACT_* of the shared branch                  */
+  int32_t renormalize;    /* must be 1: top-k weights renormalised to sum 1  */
+  int32_t act_dtype;      /* x, router weight, h, o and y: MOE_F32 | MOE_BF16 */
+  int32_t w_dtype;        /* routed W13 / W2                                 */
+  int32_t shared_w_dtype; /* shared W13s / W2s                               */
+  int32_t tile_policy;    /* MOE_TILE_*                                      */
+  int32_t reserved;       /* must be 0                                       */
+} moe_problem_t;
+
+/*
+ * moe_route -- router logits and top-k softmax gating.
+ *   logits = x . Wr^T accumulated in fp32 ("Qwen 3.5 MoE on Ironwood", model
+ *   architecture: the router projects the token and takes a softmax; the CANN
+ *   Qwen3-MoE page feeds the gate fp32 activations), then per token the k
+ *   largest logits in descending order, equal values going to the lower expert
+ *   index, weighted w_j = exp(l_j - l_0) / sum_m exp(l_m - l_0): the
+ *   renormalised top-k of the softmax, done as one fused op as on the CANN
+ *   Qwen3-MoE page (fused top-k softmax).
+ *   x        [T, D] act dtype           (unused if logits_given)
+ *   w_router [E, D] act dtype           (unused if logits_given)
+ *   logits   [T, E] fp32: written, or read when logits_given != 0
+ *   topk_idx [T, k] int32 written;  topk_w [T, k] fp32 written
+ */
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_router,
+                       float* logits, int32_t logits_given, int32_t* topk_idx,
+                       float* topk_w, void* stream);
+
+/*
+ * moe_permute -- per-expert token counts and the stable expert-major
+ * permutation ("init routing" and "compute expert tokens" on the CANN
+ * Qwen3-MoE page; the contiguous permuted buffer of the SparseCore gather on
+ * the Ironwood page, MoE track).
+ *   topk_idx    [T, k] int32, each row k distinct ids in [0, E)
+ *   counts      [E]    rows routed to each expert
+ *   offsets     [E+1]  exclusive prefix sum of counts (offsets[E] = T*k)
+ *   row_token   [T*k]  token of each sorted row; rows of one expert are in
+ *                      ascending token order
+ *   row_of_slot [T*k]  sorted row of assignment (t, j) at index t*k + j
+ *   ws / ws_bytes      scratch of at least moe_permute_workspace_size bytes
+ * Deterministic: no order-dependent atomics.  Ids outside [0, E) are a
+ * caller error: they are dropped (row_of_slot = -1) and counts then sum to
+ * less than T*k; repeated ids within a row are a caller error too.
+ */
+moe_status_t moe_permute_workspace_size(const moe_problem_t* p, size_t* bytes);
+moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
+                         int32_t* offsets, int32_t* row_token, int32_t* row_of_slot,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn -- grouped gated expert FFN over n_groups experts.
+ *   For group g and its rows r in [offsets[g], offsets[g+1]):
+ *     [gate | up] = A_r . W13[g]^T  (x s13[g] after the reduction for fp8),
+ *     h_r = act(gate) * up,  out_r = h_r . W2[g]^T  (x s2[g] for fp8)
+ *   ("CANN Qwen3-MoE", MoE TP compute decomposition: x = down(SiLU(gate(x)) *
+ *   up(x)) with gate/up merged into w13; grouped matmul over many experts in
+ *   one call; "Gemma-4 model optimisation report" section 2 for GEGLU.)
+ *   The problem's D, I, act, act_dtype, w_dtype and tile_policy describe this
+ *   call (pass I = I_shared and act = act_shared to run a shared branch as one
+ *   group with offsets {0, T} and row_token = NULL).
+ *   a         [*, D] act dtype: A_r = a[row_token[r]] if row_token, else a[r]
+ *   row_token [rows] int32 or NULL
+ *   offsets   [n_groups+1] int32 device array, offsets[n_groups] <= rows_upper_bound
+ *   w13 [n_groups, 2I, D], w2 [n_groups, D, I] (w_dtype); s13 [n_groups, 2I],
+ *   s2 [n_groups, D] fp32, required for fp8 and ignored otherwise
+ *   h   [rows_upper_bound, I] act dtype (written; intermediate)
+ *   out [rows_upper_bound, D] act dtype (written)
+ *   rows_upper_bound  host-known bound on offsets[n_groups]; it sizes the grid
+ *   ws / ws_bytes     scratch of at least moe_grouped_ffn_workspace_size bytes
+ */
+moe_status_t moe_grouped_ffn_workspace_size(const moe_problem_t* p, int32_t n_groups,
+                                            int32_t rows_upper_bound, size_t* bytes);
+moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t rows_upper_bound,
+                             const void* a, const int32_t* row_token, const int32_t* offsets,
+                             const void* w13, const float* s13, const void* w2, const float* s2,
+                             void* h, void* out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine -- unpermute and routing-weighted sum ("finalize routing" on the
+ * CANN Qwen3-MoE page; the unpermute + local reduce of the Ironwood page's MoE
+ * track), plus the shared branch:
+ *   y[t] = sum_{j<k} topk_w[t,j] * o_perm[row_of_slot[t*k+j]] + shared_out[t]
+ *   accumulated in fp32 in slot order, rounded once to the act dtype.
+ *   o_perm [T*k, D], shared_out [T, D] or NULL, y [T, D]: act dtype.
+ *   Assignments with row_of_slot < 0 contribute nothing.
+ */
+moe_status_t moe_combine(const moe_problem_t* p, const void* o_perm, const int32_t* row_of_slot,
+                         const float* topk_w, const void* shared_out, void* y, void* stream);
+
+/* Arguments of the fused layer.  Optional outputs (NULL = not wanted) are
+ * written when given; logits_in (nullable) replaces the router product. */
+typedef struct moe_layer_args {
+  const void* x;            /* [T, D] act dtype                          */
+  const void* w_router;     /* [E, D] act dtype (unused with logits_in)  */
+  const float* logits_in;   /* [T, E] fp32 or NULL                        */
+  const void* w13;          /* [E, 2I, D]                                 */
+  const float* s13;         /* [E, 2I] (fp8 only)                         */
+  const void* w2;           /* [E, D, I]                                  */
+  const float* s2;          /* [E, D]  (fp8 only)                         */
+  const void* w13_shared;   /* [2I_shared, D]  (NULL iff I_shared == 0)   */
+  const float* s13_shared;  /* [2I_shared]     (fp8 only)                 */
+  const void* w2_shared;    /* [D, I_shared]                              */
+  const float* s2_shared;   /* [D]             (fp8 only)                 */
+  void* y;                  /* [T, D] act dtype, written                  */
+  float* logits_out;        /* [T, E] optional                            */
+  int32_t* topk_idx_out;    /* [T, k] optional                            */
+  float* topk_w_out;        /* [T, k] optional                            */
+  int32_t* counts_out;      /* [E]    optional                            */
+  int32_t* offsets_out;     /* [E+1]  optional                            */
+  int32_t* row_token_out;   /* [T*k]  optional                            */
+  int32_t* row_of_slot_out; /* [T*k]  optional                            */
+} moe_layer_args_t;
+
+/*
+ * moe_layer -- the whole layer, every step enqueued on one stream with no
+ * host synchronisation: route -> permute -> grouped FFN (routed experts and the
+ * shared branch in the same launches) -> combine.  The workspace holds every
+ * intermediate (logits, routing metadata, h, o); its size depends only on the
+ * problem.
+ */
+moe_status_t moe_layer_workspace_size(const moe_problem_t* p, size_t* bytes);
+moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* args, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* moe_status_string(moe_status_t status);
+
+/*
+ * Per-stage kernel timing with HIP events, for measurement.  While enabled,
+ * moe_layer records an event pair around each stage on its stream.
+ * moe_timing_read waits for the recorded events, adds each stage's elapsed
+ * time (ms) and launch count into ms[stage] / launches[stage] for
+ * stage < n_stages, and clears the record.  Stage names: moe_stage_name.
+ * Not thread-safe; meant for a single benchmarking thread.
+ */
+moe_status_t moe_timing_enable(int32_t on);
+moe_status_t moe_timing_read(double* ms, int32_t* launches, int32_t n_stages);
+int32_t moe_stage_count(void);
+const char* moe_stage_name(int32_t stage);
+
+/*
+ * Diagnostic: decode n (a multiple of 8) fp8 e4m3fn codes to bf16 bit
+ * patterns with the exact device routine the grouped FFN uses for fp8
+ * weights, so the hardware conversion can be checked code by code against the
+ * format definition.  codes [n] uint8, out [n] uint16 (device pointers).
+ */
+moe_status_t moe_debug_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int32_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -4,11 +4,12 @@
 (same entry-point names as include/moe.h).  It is imported lazily so that the
 pure-host helpers (e.g. `costmodel`) work without the built library.
 """
+import importlib
+
 __all__ = ["binding", "costmodel"]
 
 
 def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

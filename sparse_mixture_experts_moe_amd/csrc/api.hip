@@ -1,0 +1,613 @@
+// C ABI of the MoE layer: validation, workspace planning, tile policy, launch
+// order and per-stage event timing.  See include/moe.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+size_t align_up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+size_t dt_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
+
+bool act_ok(int a) { return a == MOE_ACT_SILU || a == MOE_ACT_GELU_TANH; }
+bool dt_ok(int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_FP8_E4M3FN; }
+
+bool combo_ok(int act_dt, int w_dt) {
+  if (act_dt == MOE_F32) return w_dt == MOE_F32;
+  if (act_dt == MOE_BF16) return w_dt == MOE_BF16 || w_dt == MOE_FP8_E4M3FN;
+  return false;
+}
+
+// Checks common to every entry point.
+moe_status_t check_problem(const moe_problem_t* p, bool need_ffn, bool need_router) {
+  if (!p) return MOE_ERR_NULL;
+  if (p->T < 0 || p->D <= 0 || p->D % 64 || p->E < 1 || p->E > 1024) return MOE_ERR_SHAPE;
+  if (need_router && (p->k < 1 || p->k > 32 || p->k > p->E)) return MOE_ERR_SHAPE;
+  if (need_ffn && (p->I <= 0 || p->I % 64 || p->I_shared < 0 || p->I_shared % 64))
+    return MOE_ERR_SHAPE;
+  const int64_t Tk = static_cast<int64_t>(p->T) * std::max(p->k, 1);
+  const int64_t wide = std::max<int64_t>({p->D, p->I, p->I_shared, p->E});
+  if (Tk >= (int64_t(1) << 31) || (Tk + p->T) * wide >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  if (!dt_ok(p->act_dtype) || !dt_ok(p->w_dtype) || !dt_ok(p->shared_w_dtype)) return MOE_ERR_DTYPE;
+  if (!act_ok(p->act) || !act_ok(p->act_shared)) return MOE_ERR_DTYPE;
+  if (p->tile_policy < MOE_TILE_AUTO || p->tile_policy > MOE_TILE_LDS) return MOE_ERR_DTYPE;
+  if (p->act_dtype == MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
+  if (need_ffn && !combo_ok(p->act_dtype, p->w_dtype)) return MOE_ERR_UNSUPPORTED;
+  if (need_ffn && p->I_shared && !combo_ok(p->act_dtype, p->shared_w_dtype))
+    return MOE_ERR_UNSUPPORTED;
+  if (p->renormalize != 1 || p->reserved != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- tile policy
+struct Plan {
+  bool tiled;  // LDS-tiled kernel
+  int mt;      // stream kernel: 16-row chunks per m-tile
+  int bm;      // rows per m-tile
+};
+
+constexpr bool kTiledReady = false;
+
+Plan make_plan(const moe_problem_t* p, double mean_rows) {
+  const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16;
+  int policy = p->tile_policy;
+  if (policy == MOE_TILE_AUTO) policy = (tiled_ok && mean_rows > 48.0) ? MOE_TILE_LDS : MOE_TILE_STREAM;
+  if (policy == MOE_TILE_LDS && tiled_ok) return Plan{true, 0, tiled_bm()};
+  int mt = mean_rows <= 4.0 ? 1 : mean_rows <= 12.0 ? 2 : 4;
+  mt = std::min(mt, stream_max_mt(p->act_dtype));
+  return Plan{false, mt, 16 * mt};
+}
+
+int routed_tile_ub(int64_t rows, int groups, int bm) {
+  return static_cast<int>(std::min<int64_t>(groups, rows) + rows / bm);
+}
+
+int blocks_per_m(const Plan& pl, bool gated, int n_out) {
+  if (pl.tiled) return tiled_blocks_n(gated, n_out);
+  return (stream_waves_n(gated, n_out) + 3) / 4;
+}
+
+void finish_grid(GArgs& g, const Plan& pl, bool gated) {
+  int b = 0;
+  for (int i = 0; i < g.nsets; ++i) {
+    GSet& S = g.s[i];
+    S.blocks_per_m = blocks_per_m(pl, gated, S.n_out);
+    S.block0 = b;
+    S.bm = pl.bm;
+    b += S.m_slots * S.blocks_per_m;
+  }
+  g.total_blocks = b;
+}
+
+hipError_t run_gemm(const GArgs& g, const Plan& pl, bool gated, int a_dt, int w_dt, int o_dt,
+                    hipStream_t s) {
+  if (pl.tiled) return launch_tiled_gemm(g, gated, w_dt, o_dt, s);
+  return launch_stream_gemm(g, pl.mt, gated, a_dt, w_dt, o_dt, s);
+}
+
+// ---------------------------------------------------------------- timing
+enum Stage { ST_ROUTER = 0, ST_TOPK, ST_PERMUTE, ST_TILES, ST_FFN1, ST_FFN2, ST_COMBINE, ST_COUNT };
+const char* kStageNames[ST_COUNT] = {"router_gemm", "topk_softmax", "permute", "tile_table",
+                                     "ffn1_gate_up_act", "ffn2_down", "combine"};
+
+struct TimingRec {
+  int stage;
+  hipEvent_t a, b;
+};
+bool g_timing = false;
+std::vector<TimingRec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+struct StageScope {
+  int stage;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  StageScope(int st, hipStream_t st_s) : stage(st), s(st_s) {
+    if (g_timing && (a = take_event()) && hipEventRecord(a, s) != hipSuccess) {
+      g_pool.push_back(a);
+      a = nullptr;
+    }
+  }
+  ~StageScope() {
+    if (!a) return;
+    hipEvent_t b = take_event();
+    if (!b) {
+      g_pool.push_back(a);
+      return;
+    }
+    if (hipEventRecord(b, s) != hipSuccess) {
+      g_pool.push_back(a);
+      g_pool.push_back(b);
+      return;
+    }
+    g_recs.push_back(TimingRec{stage, a, b});
+  }
+};
+
+#define MOE_LAUNCH(expr)                                   \
+  do {                                                     \
+    if ((expr) != hipSuccess) return MOE_ERR_LAUNCH;       \
+  } while (0)
+
+// ---------------------------------------------------------------- workspace layouts
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+struct LayerLayout {
+  size_t logits, idx, w, counts, offsets, row_token, row_of_slot, blk, rank, tiles, ntiles;
+  size_t h, h_sh, o, o_sh, total;
+  int tile_ub;
+  Plan plan;
+};
+
+LayerLayout layer_layout(const moe_problem_t* p) {
+  LayerLayout L{};
+  const int64_t T = p->T, Tk = T * p->k, E = p->E;
+  const size_t a = dt_bytes(p->act_dtype);
+  L.plan = make_plan(p, E ? static_cast<double>(Tk) / E : 0.0);
+  L.tile_ub = routed_tile_ub(Tk, p->E, L.plan.bm);
+  Carve c;
+  L.logits = c.take(T * E * 4);
+  L.idx = c.take(Tk * 4);
+  L.w = c.take(Tk * 4);
+  L.counts = c.take(E * 4);
+  L.offsets = c.take((E + 1) * 4);
+  L.row_token = c.take(Tk * 4);
+  L.row_of_slot = c.take(Tk * 4);
+  L.blk = c.take(static_cast<size_t>(perm_blocks(p->T)) * E * 4);
+  L.rank = c.take(Tk * 4);
+  L.tiles = c.take(static_cast<size_t>(L.tile_ub) * sizeof(GTile));
+  L.ntiles = c.take(16);
+  L.h = c.take(Tk * p->I * a);
+  L.h_sh = c.take(T * p->I_shared * a);
+  L.o = c.take(Tk * p->D * a);
+  L.o_sh = c.take(p->I_shared ? T * p->D * a : 0);
+  L.total = c.off;
+  return L;
+}
+
+struct PermLayout {
+  size_t blk, rank, total;
+};
+PermLayout perm_layout(const moe_problem_t* p) {
+  PermLayout L{};
+  Carve c;
+  L.blk = c.take(static_cast<size_t>(perm_blocks(p->T)) * p->E * 4);
+  L.rank = c.take(static_cast<size_t>(p->T) * p->k * 4);
+  L.total = c.off;
+  return L;
+}
+
+// router product through the plain (ungated) grouped GEMM: one dense group.
+hipError_t launch_router(const moe_problem_t* p, const void* x, const void* wr, float* logits,
+                         hipStream_t s) {
+  const double dummy_rows = p->T;  // the router is one group of all T rows
+  const Plan pl = make_plan(p, dummy_rows);
+  GArgs g{};
+  g.nsets = 1;
+  GSet& S = g.s[0];
+  S.K = p->D;
+  S.a_rows = p->T;
+  S.a = x;
+  S.lda = p->D;
+  S.w = wr;
+  S.NB = p->E;
+  S.n_out = p->E;
+  S.out = logits;
+  S.ldo = p->E;
+  S.rows = p->T;
+  S.m_slots = (p->T + pl.bm - 1) / pl.bm;
+  finish_grid(g, pl, false);
+  return run_gemm(g, pl, false, p->act_dtype, p->act_dtype, MOE_F32, s);
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+extern "C" {
+
+const char* moe_status_string(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "null pointer";
+    case MOE_ERR_SHAPE: return "size out of the supported range";
+    case MOE_ERR_DTYPE: return "unknown dtype, activation or policy code";
+    case MOE_ERR_UNSUPPORTED: return "unsupported combination";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_LAUNCH: return "kernel launch or HIP runtime call failed";
+  }
+  return "unknown status";
+}
+
+moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_router, float* logits,
+                       int32_t logits_given, int32_t* topk_idx, float* topk_w, void* stream) {
+  moe_status_t st = check_problem(p, false, true);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_idx || !topk_w || (!logits_given && (!x || !w_router))) return MOE_ERR_NULL;
+  if (p->act_dtype == MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
+  if (p->T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!logits_given) {
+    StageScope sc(ST_ROUTER, s);
+    MOE_LAUNCH(launch_router(p, x, w_router, logits, s));
+  }
+  StageScope sc(ST_TOPK, s);
+  MOE_LAUNCH(launch_topk_softmax(logits, p->T, p->E, p->k, topk_idx, topk_w, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_permute_workspace_size(const moe_problem_t* p, size_t* bytes) {
+  moe_status_t st = check_problem(p, false, true);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = perm_layout(p).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
+                         int32_t* offsets, int32_t* row_token, int32_t* row_of_slot, void* ws,
+                         size_t ws_bytes, void* stream) {
+  moe_status_t st = check_problem(p, false, true);
+  if (st != MOE_OK) return st;
+  if (!topk_idx || !counts || !offsets || !row_token || !row_of_slot) return MOE_ERR_NULL;
+  const PermLayout L = perm_layout(p);
+  if (L.total && !ws) return MOE_ERR_NULL;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (p->T == 0) return MOE_OK;
+  char* w = static_cast<char*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageScope sc(ST_PERMUTE, s);
+  MOE_LAUNCH(launch_permute(topk_idx, p->T, p->k, p->E, reinterpret_cast<int32_t*>(w + L.blk),
+                            reinterpret_cast<int32_t*>(w + L.rank), counts, offsets, row_token,
+                            row_of_slot, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_grouped_ffn_workspace_size(const moe_problem_t* p, int32_t n_groups,
+                                            int32_t rows_upper_bound, size_t* bytes) {
+  moe_status_t st = check_problem(p, true, false);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_NULL;
+  if (n_groups < 1 || n_groups > 1024 || rows_upper_bound < 0) return MOE_ERR_SHAPE;
+  const Plan pl = make_plan(p, static_cast<double>(rows_upper_bound) / n_groups);
+  Carve c;
+  c.take(static_cast<size_t>(routed_tile_ub(rows_upper_bound, n_groups, pl.bm)) * sizeof(GTile));
+  c.take(16);
+  *bytes = c.off;
+  return MOE_OK;
+}
+
+moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t rows_upper_bound,
+                             const void* a, const int32_t* row_token, const int32_t* offsets,
+                             const void* w13, const float* s13, const void* w2, const float* s2,
+                             void* h, void* out, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  moe_status_t st = moe_grouped_ffn_workspace_size(p, n_groups, rows_upper_bound, &need);
+  if (st != MOE_OK) return st;
+  if (!a || !offsets || !w13 || !w2 || !h || !out || !ws) return MOE_ERR_NULL;
+  if (p->w_dtype == MOE_FP8_E4M3FN && (!s13 || !s2)) return MOE_ERR_NULL;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (rows_upper_bound == 0) return MOE_OK;
+  const Plan pl = make_plan(p, static_cast<double>(rows_upper_bound) / n_groups);
+  const int tile_ub = routed_tile_ub(rows_upper_bound, n_groups, pl.bm);
+  char* w = static_cast<char*>(ws);
+  Carve c;
+  GTile* tiles = reinterpret_cast<GTile*>(w + c.take(static_cast<size_t>(tile_ub) * sizeof(GTile)));
+  int32_t* ntiles = reinterpret_cast<int32_t*>(w + c.take(16));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool fp8 = p->w_dtype == MOE_FP8_E4M3FN;
+  {
+    StageScope sc(ST_TILES, s);
+    MOE_LAUNCH(launch_build_tiles(offsets, n_groups, pl.bm, rows_upper_bound, tile_ub, tiles,
+                                  ntiles, s));
+  }
+  GArgs g1{};
+  g1.nsets = 1;
+  {
+    GSet& S = g1.s[0];
+    S.K = p->D;
+    S.a_rows = row_token ? p->T : rows_upper_bound;
+    if (row_token && p->T <= 0) return MOE_ERR_SHAPE;
+    S.a = a;
+    S.gather = row_token;
+    S.lda = p->D;
+    S.w = w13;
+    S.scale = fp8 ? s13 : nullptr;
+    S.w_gstride = static_cast<int64_t>(2) * p->I * p->D;
+    S.s_gstride = 2 * p->I;
+    S.NB = 2 * p->I;
+    S.n_out = p->I;
+    S.act = p->act;
+    S.out = h;
+    S.ldo = p->I;
+    S.tiles = tiles;
+    S.n_tiles = ntiles;
+    S.m_slots = tile_ub;
+  }
+  finish_grid(g1, pl, true);
+  GArgs g2 = g1;
+  {
+    GSet& S = g2.s[0];
+    S.K = p->I;
+    S.a_rows = rows_upper_bound;
+    S.a = h;
+    S.gather = nullptr;
+    S.lda = p->I;
+    S.w = w2;
+    S.scale = fp8 ? s2 : nullptr;
+    S.w_gstride = static_cast<int64_t>(p->D) * p->I;
+    S.s_gstride = p->D;
+    S.NB = p->D;
+    S.n_out = p->D;
+    S.out = out;
+    S.ldo = p->D;
+  }
+  finish_grid(g2, pl, false);
+  {
+    StageScope sc(ST_FFN1, s);
+    MOE_LAUNCH(run_gemm(g1, pl, true, p->act_dtype, p->w_dtype, p->act_dtype, s));
+  }
+  {
+    StageScope sc(ST_FFN2, s);
+    MOE_LAUNCH(run_gemm(g2, pl, false, p->act_dtype, p->w_dtype, p->act_dtype, s));
+  }
+  return MOE_OK;
+}
+
+moe_status_t moe_combine(const moe_problem_t* p, const void* o_perm, const int32_t* row_of_slot,
+                         const float* topk_w, const void* shared_out, void* y, void* stream) {
+  moe_status_t st = check_problem(p, false, true);
+  if (st != MOE_OK) return st;
+  if (!o_perm || !row_of_slot || !topk_w || !y) return MOE_ERR_NULL;
+  if (p->act_dtype == MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
+  if (p->T == 0) return MOE_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageScope sc(ST_COMBINE, s);
+  MOE_LAUNCH(launch_combine(o_perm, row_of_slot, topk_w, shared_out, p->T, p->D, p->k,
+                            p->act_dtype, y, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_workspace_size(const moe_problem_t* p, size_t* bytes) {
+  moe_status_t st = check_problem(p, true, true);
+  if (st != MOE_OK) return st;
+  if (!bytes) return MOE_ERR_NULL;
+  *bytes = layer_layout(p).total;
+  return MOE_OK;
+}
+
+moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* ws, size_t ws_bytes,
+                       void* stream) {
+  moe_status_t st = check_problem(p, true, true);
+  if (st != MOE_OK) return st;
+  if (!A || !A->x || !A->w13 || !A->w2 || !A->y) return MOE_ERR_NULL;
+  if (!A->logits_in && !A->w_router) return MOE_ERR_NULL;
+  if (p->w_dtype == MOE_FP8_E4M3FN && (!A->s13 || !A->s2)) return MOE_ERR_NULL;
+  if (p->I_shared) {
+    if (!A->w13_shared || !A->w2_shared) return MOE_ERR_NULL;
+    if (p->shared_w_dtype == MOE_FP8_E4M3FN && (!A->s13_shared || !A->s2_shared)) return MOE_ERR_NULL;
+  }
+  const LayerLayout L = layer_layout(p);
+  if (!ws) return MOE_ERR_NULL;
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (p->T == 0) return MOE_OK;
+
+  char* w = static_cast<char*>(ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  auto pick = [&](auto* user, size_t off) {
+    using Ptr = decltype(user);
+    return user ? user : reinterpret_cast<Ptr>(w + off);
+  };
+  float* logits = A->logits_in ? const_cast<float*>(A->logits_in) : pick(A->logits_out, L.logits);
+  int32_t* idx = pick(A->topk_idx_out, L.idx);
+  float* tw = pick(A->topk_w_out, L.w);
+  int32_t* counts = pick(A->counts_out, L.counts);
+  int32_t* offsets = pick(A->offsets_out, L.offsets);
+  int32_t* row_token = pick(A->row_token_out, L.row_token);
+  int32_t* row_of_slot = pick(A->row_of_slot_out, L.row_of_slot);
+  GTile* tiles = reinterpret_cast<GTile*>(w + L.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(w + L.ntiles);
+  void* h = w + L.h;
+  void* h_sh = w + L.h_sh;
+  void* o = w + L.o;
+  void* o_sh = w + L.o_sh;
+  const int64_t Tk = static_cast<int64_t>(p->T) * p->k;
+  const Plan& pl = L.plan;
+
+  // 1. router logits (fp32) and top-k softmax
+  if (!A->logits_in) {
+    StageScope sc(ST_ROUTER, s);
+    MOE_LAUNCH(launch_router(p, A->x, A->w_router, logits, s));
+  }
+  {
+    StageScope sc(ST_TOPK, s);
+    MOE_LAUNCH(launch_topk_softmax(logits, p->T, p->E, p->k, idx, tw, s));
+  }
+  // 2. permutation and the M-tile table
+  {
+    StageScope sc(ST_PERMUTE, s);
+    MOE_LAUNCH(launch_permute(idx, p->T, p->k, p->E, reinterpret_cast<int32_t*>(w + L.blk),
+                              reinterpret_cast<int32_t*>(w + L.rank), counts, offsets, row_token,
+                              row_of_slot, s));
+  }
+  {
+    StageScope sc(ST_TILES, s);
+    MOE_LAUNCH(launch_build_tiles(offsets, p->E, pl.bm, static_cast<int>(Tk), L.tile_ub, tiles,
+                                  ntiles, s));
+  }
+  // 3. grouped FFN: shared branch (dense rows) and routed experts in the same launches
+  const bool fp8 = p->w_dtype == MOE_FP8_E4M3FN;
+  const bool fp8s = p->shared_w_dtype == MOE_FP8_E4M3FN;
+  GArgs g1{};
+  int si = 0;
+  if (p->I_shared) {
+    GSet& S = g1.s[si++];
+    S.K = p->D;
+    S.a_rows = p->T;
+    S.a = A->x;
+    S.lda = p->D;
+    S.w = A->w13_shared;
+    S.scale = fp8s ? A->s13_shared : nullptr;
+    S.NB = 2 * p->I_shared;
+    S.n_out = p->I_shared;
+    S.act = p->act_shared;
+    S.out = h_sh;
+    S.ldo = p->I_shared;
+    S.rows = p->T;
+    S.m_slots = (p->T + pl.bm - 1) / pl.bm;
+  }
+  {
+    GSet& S = g1.s[si++];
+    S.K = p->D;
+    S.a_rows = p->T;
+    S.a = A->x;
+    S.gather = row_token;
+    S.lda = p->D;
+    S.w = A->w13;
+    S.scale = fp8 ? A->s13 : nullptr;
+    S.w_gstride = static_cast<int64_t>(2) * p->I * p->D;
+    S.s_gstride = 2 * p->I;
+    S.NB = 2 * p->I;
+    S.n_out = p->I;
+    S.act = p->act;
+    S.out = h;
+    S.ldo = p->I;
+    S.tiles = tiles;
+    S.n_tiles = ntiles;
+    S.m_slots = L.tile_ub;
+  }
+  g1.nsets = si;
+  finish_grid(g1, pl, true);
+  GArgs g2 = g1;
+  si = 0;
+  if (p->I_shared) {
+    GSet& S = g2.s[si++];
+    S.K = p->I_shared;
+    S.a_rows = p->T;
+    S.a = h_sh;
+    S.lda = p->I_shared;
+    S.w = A->w2_shared;
+    S.scale = fp8s ? A->s2_shared : nullptr;
+    S.NB = p->D;
+    S.n_out = p->D;
+    S.out = o_sh;
+    S.ldo = p->D;
+  }
+  {
+    GSet& S = g2.s[si++];
+    S.K = p->I;
+    S.a_rows = static_cast<int32_t>(Tk);
+    S.a = h;
+    S.gather = nullptr;
+    S.lda = p->I;
+    S.w = A->w2;
+    S.scale = fp8 ? A->s2 : nullptr;
+    S.w_gstride = static_cast<int64_t>(p->D) * p->I;
+    S.s_gstride = p->D;
+    S.NB = p->D;
+    S.n_out = p->D;
+    S.out = o;
+    S.ldo = p->D;
+  }
+  finish_grid(g2, pl, false);
+  if (fp8 != fp8s && p->I_shared) {
+    // one launch covers one weight dtype: run the two sets separately
+    for (int i = 0; i < 2; ++i) {
+      GArgs a1{}, a2{};
+      a1.nsets = a2.nsets = 1;
+      a1.s[0] = g1.s[i];
+      a2.s[0] = g2.s[i];
+      finish_grid(a1, pl, true);
+      finish_grid(a2, pl, false);
+      const int wdt = i == 0 ? p->shared_w_dtype : p->w_dtype;
+      {
+        StageScope sc(ST_FFN1, s);
+        MOE_LAUNCH(run_gemm(a1, pl, true, p->act_dtype, wdt, p->act_dtype, s));
+      }
+      {
+        StageScope sc(ST_FFN2, s);
+        MOE_LAUNCH(run_gemm(a2, pl, false, p->act_dtype, wdt, p->act_dtype, s));
+      }
+    }
+  } else {
+    {
+      StageScope sc(ST_FFN1, s);
+      MOE_LAUNCH(run_gemm(g1, pl, true, p->act_dtype, p->w_dtype, p->act_dtype, s));
+    }
+    {
+      StageScope sc(ST_FFN2, s);
+      MOE_LAUNCH(run_gemm(g2, pl, false, p->act_dtype, p->w_dtype, p->act_dtype, s));
+    }
+  }
+  // 4. unpermute + weighted combine + shared branch
+  {
+    StageScope sc(ST_COMBINE, s);
+    MOE_LAUNCH(launch_combine(o, row_of_slot, tw, p->I_shared ? o_sh : nullptr, p->T, p->D, p->k,
+                              p->act_dtype, A->y, s));
+  }
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- timing ABI
+moe_status_t moe_timing_enable(int32_t on) {
+  g_timing = on != 0;
+  return MOE_OK;
+}
+
+moe_status_t moe_timing_read(double* ms, int32_t* launches, int32_t n_stages) {
+  if ((!ms || !launches) && n_stages > 0) return MOE_ERR_NULL;
+  moe_status_t st = MOE_OK;
+  for (const TimingRec& r : g_recs) {
+    float t = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+      st = MOE_ERR_LAUNCH;
+    if (r.stage < n_stages) {
+      ms[r.stage] += t;
+      launches[r.stage] += 1;
+    }
+    g_pool.push_back(r.a);
+    g_pool.push_back(r.b);
+  }
+  g_recs.clear();
+  return st;
+}
+
+int32_t moe_stage_count(void) { return ST_COUNT; }
+
+const char* moe_stage_name(int32_t stage) {
+  return (stage >= 0 && stage < ST_COUNT) ? kStageNames[stage] : "unknown";
+}
+
+moe_status_t moe_debug_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int32_t n, void* stream) {
+  if (!codes || !out) return MOE_ERR_NULL;
+  if (n < 0 || n % 8) return MOE_ERR_SHAPE;
+  MOE_LAUNCH(launch_fp8_decode(codes, out, n, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+}  // extern "C"

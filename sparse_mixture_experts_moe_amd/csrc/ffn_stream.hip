@@ -1,0 +1,330 @@
+// Grouped expert GEMM with weights streamed from HBM straight into registers.
+//
+// Built for groups of few rows (decode-sized batches), where the expert FFN is
+// bound by reading every touched expert's weights once ("Qwen 3.5 MoE on
+// Ironwood", roofline section: decode is HBM-bound at about 1 FLOP/byte; the
+// "Ling-2.6-1T with SGLang-JAX" page, section 1, HBM weight-movement bound).
+//
+// Work decomposition: each 64-wide wavefront owns one M-tile of a group (up to
+// 16*MT sorted rows) and 64 weight rows (4 MFMA fragments of 16).  For the
+// fused gate/up projection those are 32 gate rows and the 32 matching up rows,
+// so SiLU(gate)*up (or tanh-GELU) is applied in registers and only h is stored
+// -- the packed gate/up tile of GMM v2 on the Ironwood page (MoE track), without
+// an HBM round trip for the two halves.  Every weight element is loaded by
+// exactly one wavefront per M-tile; the activation rows are gathered through
+// the permutation (the SparseCore gather of the Ironwood page, fused into the
+// A-operand load instead of a materialised permuted copy).
+//
+// The K loop is software-pipelined over two register stages of 32*U elements.
+// Lane group q = lane/16 holds a contiguous run of 8*U K-elements of its row,
+// used 8 at a time by successive MFMAs; A and B use the same K assignment, so
+// each MFMA still contracts matching elements.
+//
+// fp8 e4m3fn weights are decoded exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8,
+// scale 1) and their per-output-channel fp32 scale is applied after the
+// reduction ("Ling-2.6-1T with SGLang-JAX", section 5, per-channel scaling).
+// fp32 problems use fp32 MFMA (16x16x4), never a reduced precision.
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int NF = 4;            // 16-row weight fragments per wavefront
+constexpr int WAVES = 4;         // wavefronts per block (consecutive N tiles)
+
+template <int DT> struct Elt;
+template <> struct Elt<DT_F32> { static constexpr int bytes = 4; };
+template <> struct Elt<DT_BF16> { static constexpr int bytes = 2; };
+template <> struct Elt<DT_FP8> { static constexpr int bytes = 1; };
+
+// uint4 vectors holding 8*U elements of dtype DT
+template <int DT, int U> struct VecCount {
+  static constexpr int n = (8 * U * Elt<DT>::bytes) / 16;
+};
+
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(lo), 1.0f, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(lo), 1.0f, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(hi), 1.0f, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(hi), 1.0f, true);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Operand of one MFMA step (8 K-elements per lane) from the staged uint4s.
+template <int DT>
+__device__ __forceinline__ bf16x8 operand_bf16(const uint4* v, int u) {
+  if constexpr (DT == DT_BF16) {
+    return __builtin_bit_cast(bf16x8, v[u]);
+  } else {  // DT_FP8: 8 bytes of step u
+    const uint4 q = v[u >> 1];
+    return (u & 1) ? fp8x8_to_bf16x8(q.z, q.w) : fp8x8_to_bf16x8(q.x, q.y);
+  }
+}
+
+__device__ __forceinline__ float act_fn(int act, float z) {
+  if (act == ACT_SILU) return z / (1.0f + expf(-z));
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
+}
+
+// Which set / M-tile / N-block a block works on; false if it has no work.
+__device__ __forceinline__ bool resolve_block(const GArgs& g, int b, int& si, int& group, int& row0,
+                                              int& row1, int& nblk) {
+  si = (g.nsets > 1 && b >= g.s[1].block0) ? 1 : 0;
+  const GSet& S = g.s[si];
+  const int local = b - S.block0;
+  const int m = local / S.blocks_per_m;
+  nblk = local - m * S.blocks_per_m;
+  if (S.tiles) {
+    if (m >= S.n_tiles[0]) return false;
+    const GTile t = S.tiles[m];
+    group = t.group;
+    row0 = t.row0;
+    row1 = t.row1;
+  } else {
+    row0 = m * S.bm;
+    if (row0 >= S.rows) return false;
+    row1 = min(row0 + S.bm, S.rows);
+    group = 0;
+  }
+  return row1 > row0;
+}
+
+template <int MT, int U, bool GATED, int ADT, int WDT, int ODT>
+__global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs g) {
+  constexpr int AV = VecCount<ADT, U>::n;   // uint4 per lane per stage, A
+  constexpr int BV = VecCount<WDT, U>::n;   // uint4 per lane per stage, B (per fragment)
+  constexpr int KS = 32 * U;                // K elements per stage
+  int si, group, row0, row1, nblk;
+  if (!resolve_block(g, blockIdx.x, si, group, row0, row1, nblk)) return;
+  const GSet& S = g.s[si];
+  const int lane = threadIdx.x & 63;
+  const int q = lane >> 4, lr = lane & 15;
+  const int wn = nblk * WAVES + (threadIdx.x >> 6);
+  const int n_out = S.n_out;
+  const int waves_n = GATED ? n_out / 32 : (n_out + 63) / 64;
+  if (wn >= waves_n) return;
+  const int K = S.K;
+  const int nch = (row1 - row0 + 15) >> 4;  // active 16-row chunks (<= MT)
+
+  // ---- operand pointers (element offsets are per lane: row + q*8U)
+  const char* a_base = static_cast<const char*>(S.a);
+  const char* ap[MT];
+  bool av[MT];
+#pragma unroll
+  for (int mc = 0; mc < MT; ++mc) {
+    const int r = row0 + mc * 16 + lr;
+    av[mc] = mc < nch && r < row1;
+    int64_t arow = 0;
+    if (av[mc]) {
+      arow = S.gather ? S.gather[r] : r;
+      if (static_cast<uint64_t>(arow) >= static_cast<uint64_t>(S.a_rows)) {  // caller error
+        av[mc] = false;
+        arow = 0;
+      }
+    }
+    ap[mc] = a_base + (arow * S.lda + q * 8 * U) * Elt<ADT>::bytes;
+  }
+  const char* w_base = static_cast<const char*>(S.w) + group * S.w_gstride * Elt<WDT>::bytes;
+  const char* bp[NF];
+  bool bv[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    int n;
+    if (GATED) {
+      n = (f < 2 ? 0 : n_out) + wn * 32 + (f & 1) * 16 + lr;
+      bv[f] = true;
+    } else {
+      n = wn * 64 + f * 16 + lr;
+      bv[f] = n < n_out;
+      if (!bv[f]) n = 0;
+    }
+    bp[f] = w_base + (static_cast<int64_t>(n) * K + q * 8 * U) * Elt<WDT>::bytes;
+  }
+
+  f32x4 acc[MT][NF];
+#pragma unroll
+  for (int mc = 0; mc < MT; ++mc)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) acc[mc][f] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  uint4 sa0[MT][AV], sb0[NF][BV], sa1[MT][AV], sb1[NF][BV];
+
+  auto load = [&](uint4 (&sa)[MT][AV], uint4 (&sb)[NF][BV], int stage) {
+    const int64_t koff = static_cast<int64_t>(stage) * KS;
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      const uint4* p = reinterpret_cast<const uint4*>(bp[f] + koff * Elt<WDT>::bytes);
+#pragma unroll
+      for (int v = 0; v < BV; ++v) sb[f][v] = bv[f] ? p[v] : uint4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int mc = 0; mc < MT; ++mc) {
+      const uint4* p = reinterpret_cast<const uint4*>(ap[mc] + koff * Elt<ADT>::bytes);
+#pragma unroll
+      for (int v = 0; v < AV; ++v) sa[mc][v] = av[mc] ? p[v] : uint4{0, 0, 0, 0};
+    }
+  };
+
+  auto compute = [&](const uint4 (&sa)[MT][AV], const uint4 (&sb)[NF][BV]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if constexpr (ADT == DT_F32) {
+        // fp32: eight 16x16x4 MFMAs per 8 K-elements; element i of every lane
+        // group forms the K=4 slice of the i-th instruction.
+#pragma unroll
+        for (int mc = 0; mc < MT; ++mc) {
+          if (mc < nch) {
+            const float* af = reinterpret_cast<const float*>(&sa[mc][2 * u]);
+#pragma unroll
+            for (int f = 0; f < NF; ++f) {
+              const float* bf = reinterpret_cast<const float*>(&sb[f][2 * u]);
+#pragma unroll
+              for (int i = 0; i < 8; ++i)
+                acc[mc][f] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bf[i], acc[mc][f], 0, 0, 0);
+            }
+          }
+        }
+      } else {
+        bf16x8 bo[NF];
+#pragma unroll
+        for (int f = 0; f < NF; ++f) bo[f] = operand_bf16<WDT>(sb[f], u);
+#pragma unroll
+        for (int mc = 0; mc < MT; ++mc) {
+          if (mc < nch) {
+            const bf16x8 ao = __builtin_bit_cast(bf16x8, sa[mc][u]);
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+              acc[mc][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, bo[f], acc[mc][f], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
+  const int nst = K / KS;
+  load(sa0, sb0, 0);
+  for (int st = 0; st < nst; st += 2) {
+    if (st + 1 < nst) load(sa1, sb1, st + 1);
+    compute(sa0, sb0);
+    if (st + 1 < nst) {
+      if (st + 2 < nst) load(sa0, sb0, st + 2);
+      compute(sa1, sb1);
+    }
+  }
+
+  // ---- epilogue: C[row = 4*q + j][col = lr] of each 16x16 fragment
+  const float* sc = S.scale ? S.scale + group * S.s_gstride : nullptr;
+  char* out = static_cast<char*>(S.out);
+#pragma unroll
+  for (int mc = 0; mc < MT; ++mc) {
+    if (mc >= nch) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = row0 + mc * 16 + q * 4 + j;
+      if (r >= row1) continue;
+      if constexpr (GATED) {
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+          const int col = wn * 32 + f * 16 + lr;
+          float gv = acc[mc][f][j], uv = acc[mc][f + 2][j];
+          if (sc) {
+            gv *= sc[col];
+            uv *= sc[n_out + col];
+          }
+          const float h = act_fn(S.act, gv) * uv;
+          const int64_t o = static_cast<int64_t>(r) * S.ldo + col;
+          if constexpr (ODT == DT_F32) reinterpret_cast<float*>(out)[o] = h;
+          else reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16(h);
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int col = wn * 64 + f * 16 + lr;
+          if (col >= n_out) continue;
+          float v = acc[mc][f][j];
+          if (sc) v *= sc[col];
+          const int64_t o = static_cast<int64_t>(r) * S.ldo + col;
+          if constexpr (ODT == DT_F32) reinterpret_cast<float*>(out)[o] = v;
+          else reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
+template <int MT, int U, bool GATED, int ADT, int WDT, int ODT>
+hipError_t launch_one(const GArgs& g, hipStream_t s) {
+  stream_gemm_kernel<MT, U, GATED, ADT, WDT, ODT><<<g.total_blocks, 64 * WAVES, 0, s>>>(g);
+  return hipGetLastError();
+}
+
+template <int MT, bool GATED, int ADT, int WDT, int ODT>
+hipError_t pick_u(const GArgs& g, hipStream_t s) {
+  // four-step stages when every K allows and registers do (bf16/fp8 operands,
+  // at most two 16-row chunks); fp32 operands always use two-step stages
+  if constexpr (MT <= 2 && ADT != DT_F32) {
+    bool k128 = true;
+    for (int i = 0; i < g.nsets; ++i) k128 = k128 && g.s[i].K % 128 == 0;
+    if (k128) return launch_one<MT, 4, GATED, ADT, WDT, ODT>(g, s);
+  }
+  return launch_one<MT, 2, GATED, ADT, WDT, ODT>(g, s);
+}
+
+template <bool GATED, int ADT, int WDT, int ODT>
+hipError_t pick_mt(const GArgs& g, int mt, hipStream_t s) {
+  if (mt == 1) return pick_u<1, GATED, ADT, WDT, ODT>(g, s);
+  if constexpr (ADT == DT_F32) {
+    return pick_u<2, GATED, ADT, WDT, ODT>(g, s);  // fp32: at most 32-row tiles
+  } else {
+    if (mt == 2) return pick_u<2, GATED, ADT, WDT, ODT>(g, s);
+    return pick_u<4, GATED, ADT, WDT, ODT>(g, s);
+  }
+}
+
+template <bool GATED>
+hipError_t pick_types(const GArgs& g, int mt, int a_dt, int w_dt, int o_dt, hipStream_t s) {
+  if (a_dt == DT_F32 && w_dt == DT_F32 && o_dt == DT_F32)
+    return pick_mt<GATED, DT_F32, DT_F32, DT_F32>(g, mt, s);
+  if (a_dt == DT_BF16 && w_dt == DT_BF16 && o_dt == DT_BF16)
+    return pick_mt<GATED, DT_BF16, DT_BF16, DT_BF16>(g, mt, s);
+  if (a_dt == DT_BF16 && w_dt == DT_FP8 && o_dt == DT_BF16)
+    return pick_mt<GATED, DT_BF16, DT_FP8, DT_BF16>(g, mt, s);
+  if (!GATED && a_dt == DT_BF16 && w_dt == DT_BF16 && o_dt == DT_F32)
+    return pick_mt<GATED, DT_BF16, DT_BF16, DT_F32>(g, mt, s);
+  return hipErrorInvalidValue;
+}
+
+__global__ void fp8_decode_kernel(const uint8_t* __restrict__ codes, uint16_t* __restrict__ out,
+                                  int n) {
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (i >= n) return;
+  const uint2 q = *reinterpret_cast<const uint2*>(codes + i);
+  const bf16x8 v = fp8x8_to_bf16x8(q.x, q.y);
+  *reinterpret_cast<bf16x8*>(out + i) = v;
+}
+
+}  // namespace
+
+hipError_t launch_fp8_decode(const uint8_t* codes, uint16_t* out, int n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fp8_decode_kernel<<<(n / 8 + 255) / 256, 256, 0, s>>>(codes, out, n);
+  return hipGetLastError();
+}
+
+int stream_waves_n(bool gated, int n_out) { return gated ? n_out / 32 : (n_out + 63) / 64; }
+
+int stream_max_mt(int a_dtype) { return a_dtype == DT_F32 ? 2 : 4; }
+
+hipError_t launch_stream_gemm(const GArgs& g, int mt, bool gated, int a_dtype, int w_dtype,
+                              int out_dtype, hipStream_t s) {
+  if (g.total_blocks <= 0) return hipSuccess;
+  return gated ? pick_types<true>(g, mt, a_dtype, w_dtype, out_dtype, s)
+               : pick_types<false>(g, mt, a_dtype, w_dtype, out_dtype, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,197 @@
+// Deterministic expert-major permutation of the (token, slot) assignments and
+// the per-expert M-tile table of the grouped GEMM.
+//
+// Counts, their prefix sum and the stable order ("init routing" and "compute
+// expert tokens" on the "CANN Qwen3-MoE" page; the contiguous permuted buffer
+// that the SparseCore gather of the "Qwen 3.5 MoE on Ironwood" page writes) are
+// built without order-dependent atomics:
+//   1. each block of PB tokens sets, in LDS, one bit per (expert, token) pair;
+//      a token's rank inside its expert is the popcount of the bits of lower
+//      tokens, and the block's count is the popcount of the whole mask;
+//   2. one block scans the per-block counts down each expert column and then
+//      across experts (exclusive), giving every (block, expert) its base row;
+//   3. every assignment writes row = base + rank.
+// Rows of one expert are therefore in ascending token order.
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int PB = 256;                 // tokens per permutation block
+constexpr int WORDS = PB / 64;          // 64-bit mask words per expert
+constexpr int SCAN_THREADS = 1024;      // E <= 1024
+
+__global__ __launch_bounds__(PB) void perm_mask_kernel(const int32_t* __restrict__ idx, int T,
+                                                       int k, int E, int32_t* __restrict__ blk,
+                                                       int32_t* __restrict__ local_rank) {
+  extern __shared__ unsigned long long mask[];  // [E][WORDS]
+  for (int i = threadIdx.x; i < E * WORDS; i += PB) mask[i] = 0ull;
+  __syncthreads();
+  const int tl = threadIdx.x;
+  const int t = blockIdx.x * PB + tl;
+  const int w = tl >> 6;
+  const unsigned long long bit = 1ull << (tl & 63);
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[static_cast<int64_t>(t) * k + j];
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicOr(&mask[e * WORDS + w], bit);
+    }
+  }
+  __syncthreads();
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = idx[static_cast<int64_t>(t) * k + j];
+      int r = 0;
+      if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) {
+        for (int ww = 0; ww < w; ++ww) r += __popcll(mask[e * WORDS + ww]);
+        r += __popcll(mask[e * WORDS + w] & (bit - 1ull));
+      }
+      local_rank[static_cast<int64_t>(t) * k + j] = r;
+    }
+  }
+  for (int e = threadIdx.x; e < E; e += PB) {
+    int c = 0;
+#pragma unroll
+    for (int ww = 0; ww < WORDS; ++ww) c += __popcll(mask[e * WORDS + ww]);
+    blk[static_cast<int64_t>(blockIdx.x) * E + e] = c;
+  }
+}
+
+// Single block: column scans of the per-block counts (turned into base rows in
+// place), counts, and the exclusive scan over experts.
+__global__ __launch_bounds__(SCAN_THREADS) void perm_scan_kernel(int32_t* __restrict__ blk, int nb,
+                                                                 int E, int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ offsets) {
+  __shared__ int32_t sc[SCAN_THREADS];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      const int c = blk[static_cast<int64_t>(b) * E + e];
+      blk[static_cast<int64_t>(b) * E + e] = run;
+      run += c;
+    }
+    counts[e] = run;
+  }
+  sc[e] = e < E ? run : 0;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the expert totals
+  for (int off = 1; off < SCAN_THREADS; off <<= 1) {
+    const int add = e >= off ? sc[e - off] : 0;
+    __syncthreads();
+    sc[e] += add;
+    __syncthreads();
+  }
+  const int excl = sc[e] - (e < E ? run : 0);
+  if (e < E) {
+    offsets[e] = excl;
+    if (e == E - 1) offsets[E] = sc[e];
+    for (int b = 0; b < nb; ++b) blk[static_cast<int64_t>(b) * E + e] += excl;
+  }
+}
+
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ idx,
+                                                           const int32_t* __restrict__ local_rank,
+                                                           const int32_t* __restrict__ blk, int T,
+                                                           int k, int E,
+                                                           int32_t* __restrict__ row_token,
+                                                           int32_t* __restrict__ row_of_slot) {
+  const int64_t a = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (a >= static_cast<int64_t>(T) * k) return;
+  const int t = static_cast<int>(a / k);
+  const int e = idx[a];
+  if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) {
+    row_of_slot[a] = -1;
+    return;
+  }
+  const int r = blk[static_cast<int64_t>(t / PB) * E + e] + local_rank[a];
+  row_token[r] = t;
+  row_of_slot[a] = r;
+}
+
+// Single block: each group's M-tiles, groups ordered by descending row count
+// (ties by group id) so the heaviest experts start first.
+constexpr int TILE_THREADS = 1024;
+
+__device__ __forceinline__ int clamp_row(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+__global__ __launch_bounds__(TILE_THREADS) void build_tiles_kernel(const int32_t* __restrict__ offsets,
+                                                                   int G, int bm, int max_rows,
+                                                                   int max_tiles,
+                                                                   GTile* __restrict__ tiles,
+                                                                   int32_t* __restrict__ n_tiles) {
+  __shared__ int32_t ntl[TILE_THREADS];   // tiles of the group at each rank position
+  __shared__ int32_t grp[TILE_THREADS];   // group at each rank position
+  const int g = threadIdx.x;
+  int n = 0, rank = 0;
+  // group sizes from offsets clamped to [0, max_rows] (non-decreasing)
+  auto lo = [&](int i) { return clamp_row(offsets[i], 0, max_rows); };
+  auto size = [&](int i) { const int a = lo(i); return clamp_row(offsets[i + 1], a, max_rows) - a; };
+  if (g < G) {
+    n = size(g);
+    for (int o = 0; o < G; ++o) {
+      const int no = size(o);
+      rank += (no > n) || (no == n && o < g);
+    }
+  }
+  if (g < G) {
+    ntl[rank] = (n + bm - 1) / bm;
+    grp[rank] = g;
+  }
+  for (int i = G + threadIdx.x; i < TILE_THREADS; i += TILE_THREADS) ntl[i] = 0;
+  __syncthreads();
+  // inclusive scan of tiles in rank order
+  for (int off = 1; off < TILE_THREADS; off <<= 1) {
+    const int add = g >= off ? ntl[g - off] : 0;
+    __syncthreads();
+    ntl[g] += add;
+    __syncthreads();
+  }
+  if (g < G) {
+    const int gg = grp[g];
+    const int r0 = lo(gg), r1 = r0 + size(gg);
+    const int base = g > 0 ? ntl[g - 1] : 0;
+    for (int i = 0, r = r0; r < r1 && base + i < max_tiles; ++i, r += bm) {
+      GTile tl;
+      tl.group = gg;
+      tl.row0 = r;
+      tl.row1 = r + bm < r1 ? r + bm : r1;
+      tl.pad = 0;
+      tiles[base + i] = tl;
+    }
+  }
+  if (g == 0) {
+    const int total = G > 0 ? ntl[G - 1] : 0;
+    n_tiles[0] = total < max_tiles ? total : max_tiles;
+  }
+}
+
+}  // namespace
+
+int perm_blocks(int T) { return (T + PB - 1) / PB; }
+
+hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* blk, int32_t* local_rank,
+                          int32_t* counts, int32_t* offsets, int32_t* row_token,
+                          int32_t* row_of_slot, hipStream_t s) {
+  const int nb = perm_blocks(T);
+  if (nb > 0) {
+    perm_mask_kernel<<<nb, PB, sizeof(unsigned long long) * WORDS * E, s>>>(idx, T, k, E, blk,
+                                                                           local_rank);
+  }
+  perm_scan_kernel<<<1, SCAN_THREADS, 0, s>>>(blk, nb, E, counts, offsets);
+  const int64_t n = static_cast<int64_t>(T) * k;
+  if (n > 0) {
+    perm_scatter_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
+        idx, local_rank, blk, T, k, E, row_token, row_of_slot);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int bm, int max_rows,
+                              int max_tiles, GTile* tiles, int32_t* n_tiles, hipStream_t s) {
+  build_tiles_kernel<<<1, TILE_THREADS, 0, s>>>(offsets, n_groups, bm, max_rows, max_tiles, tiles,
+                                                n_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

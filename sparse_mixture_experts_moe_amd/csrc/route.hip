@@ -1,0 +1,96 @@
+// Top-k softmax gating with renormalisation, one 64-wide wavefront per token.
+//
+// Selection is an exact comparison of fp32 logits: k rounds of a wavefront
+// arg-max over (value, -expert) keys, so equal values go to the lower expert
+// index (+0 and -0 compare equal).  The weights are the renormalised top-k of
+// the softmax, w_j = exp(l_j - l_0) / sum_m exp(l_m - l_0), which is the fused
+// top-k softmax of the "CANN Qwen3-MoE" page (GMM enablement and routing
+// optimisation) and the softmax-then-top-10 router of the "Qwen 3.5 MoE on
+// Ironwood" page (model architecture) after renormalisation.
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int WAVES_PER_BLOCK = 4;
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+template <int EPL>
+__global__ __launch_bounds__(64 * WAVES_PER_BLOCK) void topk_softmax_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ idx,
+    float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * WAVES_PER_BLOCK + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + static_cast<int64_t>(t) * E;
+  float v[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? row[e] : -__builtin_inff();
+  }
+  uint32_t taken = 0;
+  float my_v = 0.f, top_v = 0.f;
+  int my_i = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E && !(taken >> j & 1u) && better(v[j], e, bv, bi)) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+    // butterfly arg-max: every lane ends with the wavefront's best key
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (r == 0) top_v = bv;
+    if (lane == r) {
+      my_v = bv;
+      my_i = bi;
+    }
+  }
+  float ex = lane < k ? expf(my_v - top_v) : 0.f;
+  float sum = ex;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if (lane < k) {
+    idx[static_cast<int64_t>(t) * k + lane] = my_i;
+    wout[static_cast<int64_t>(t) * k + lane] = ex / sum;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                               hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK), block(64 * WAVES_PER_BLOCK);
+  const int epl = (E + 63) / 64;
+  if (epl <= 1)
+    topk_softmax_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+  else if (epl <= 2)
+    topk_softmax_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+  else if (epl <= 4)
+    topk_softmax_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+  else if (epl <= 8)
+    topk_softmax_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+  else
+    topk_softmax_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+  return hipGetLastError();
+}
+
+}  // namespace moe
