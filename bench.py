@@ -43,7 +43,24 @@ def parse():
     ap.add_argument("--policy", default="auto", choices=["auto", "stream", "lds"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
+    ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
+                    help="only run 10 plain device copies of MIB MiB (counter calibration)")
     return ap.parse_args()
+
+
+def copy_calib(mib: int):
+    """Ten device-to-device copies of a known size, so HBM counters read under a
+    profiler can be scaled to bytes (FETCH_SIZE / WRITE_SIZE per dispatch vs
+    the known size)."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes": n, "copies": 10}), flush=True)
 
 
 def cpu_baseline(wl, n_tokens: int):
@@ -93,6 +110,9 @@ def cpu_baseline(wl, n_tokens: int):
 
 def main():
     args = parse()
+    if args.copy_calib:
+        copy_calib(args.copy_calib)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))

@@ -54,14 +54,20 @@ struct Plan {
   int bm;      // rows per m-tile
 };
 
-constexpr bool kTiledReady = false;
+constexpr bool kTiledReady = true;
+
+// Largest mean rows per group for which the streamed GEMM uses 32-row tiles
+// (build-time tuning knob).
+#ifndef MOE_MT2_MEAN
+#define MOE_MT2_MEAN 12.0
+#endif
 
 Plan make_plan(const moe_problem_t* p, double mean_rows) {
   const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16;
   int policy = p->tile_policy;
   if (policy == MOE_TILE_AUTO) policy = (tiled_ok && mean_rows > 48.0) ? MOE_TILE_LDS : MOE_TILE_STREAM;
   if (policy == MOE_TILE_LDS && tiled_ok) return Plan{true, 0, tiled_bm()};
-  int mt = mean_rows <= 4.0 ? 1 : mean_rows <= 12.0 ? 2 : 4;
+  int mt = mean_rows <= 4.0 ? 1 : mean_rows <= MOE_MT2_MEAN ? 2 : 4;
   mt = std::min(mt, stream_max_mt(p->act_dtype));
   return Plan{false, mt, 16 * mt};
 }
@@ -82,9 +88,33 @@ void finish_grid(GArgs& g, const Plan& pl, bool gated) {
     S.blocks_per_m = blocks_per_m(pl, gated, S.n_out);
     S.block0 = b;
     S.bm = pl.bm;
-    b += S.m_slots * S.blocks_per_m;
+    b += S.m_slots * S.blocks_per_m * std::max(1, S.ksplit);
   }
   g.total_blocks = b;
+}
+
+// The router is one dense group of T rows.  Large T: LDS-tiled GEMM.  Small T
+// (decode): streamed GEMM with the K dimension split into slices whose fp32
+// partial sums the top-k kernel adds in slice order, so enough wavefronts
+// stream the router weight.
+Plan router_plan(const moe_problem_t* p) {
+  if (kTiledReady && p->act_dtype == MOE_BF16 && p->T >= 1024 && p->tile_policy != MOE_TILE_STREAM)
+    return Plan{true, 0, tiled_bm()};
+  int mt = p->T <= 16 ? 1 : p->T <= 32 ? 2 : 4;
+  mt = std::min(mt, stream_max_mt(p->act_dtype));
+  return Plan{false, mt, 16 * mt};
+}
+
+// K slices of the router: enough work items (tiled blocks or stream
+// wavefronts) to cover the GPU, each slice a multiple of 64 and >= 256 long.
+int router_splits(const moe_problem_t* p, const Plan& pl) {
+  const int64_t m_tiles = (p->T + pl.bm - 1) / pl.bm;
+  const int64_t items = pl.tiled ? m_tiles * tiled_blocks_n(false, p->E)
+                                 : m_tiles * stream_waves_n(false, p->E);
+  int s = 1;
+  const int K = p->D;
+  while (K % (2 * s) == 0 && (K / (2 * s)) % 64 == 0 && K / (2 * s) >= 256 && items * s < 512) s *= 2;
+  return s;
 }
 
 hipError_t run_gemm(const GArgs& g, const Plan& pl, bool gated, int a_dt, int w_dt, int o_dt,
@@ -162,6 +192,7 @@ struct LayerLayout {
   size_t logits, idx, w, counts, offsets, row_token, row_of_slot, blk, rank, tiles, ntiles;
   size_t h, h_sh, o, o_sh, total;
   int tile_ub;
+  int splits;
   Plan plan;
 };
 
@@ -172,7 +203,8 @@ LayerLayout layer_layout(const moe_problem_t* p) {
   L.plan = make_plan(p, E ? static_cast<double>(Tk) / E : 0.0);
   L.tile_ub = routed_tile_ub(Tk, p->E, L.plan.bm);
   Carve c;
-  L.logits = c.take(T * E * 4);
+  L.splits = router_splits(p, router_plan(p));
+  L.logits = c.take(T * E * 4 * L.splits);
   L.idx = c.take(Tk * 4);
   L.w = c.take(Tk * 4);
   L.counts = c.take(E * 4);
@@ -203,11 +235,11 @@ PermLayout perm_layout(const moe_problem_t* p) {
   return L;
 }
 
-// router product through the plain (ungated) grouped GEMM: one dense group.
-hipError_t launch_router(const moe_problem_t* p, const void* x, const void* wr, float* logits,
-                         hipStream_t s) {
-  const double dummy_rows = p->T;  // the router is one group of all T rows
-  const Plan pl = make_plan(p, dummy_rows);
+// router product through the plain (ungated) grouped GEMM: one dense group,
+// written as `splits` partial sums part[s][T][E].
+hipError_t launch_router(const moe_problem_t* p, const void* x, const void* wr, float* part,
+                         int splits, hipStream_t s) {
+  const Plan pl = router_plan(p);
   GArgs g{};
   g.nsets = 1;
   GSet& S = g.s[0];
@@ -218,10 +250,12 @@ hipError_t launch_router(const moe_problem_t* p, const void* x, const void* wr, 
   S.w = wr;
   S.NB = p->E;
   S.n_out = p->E;
-  S.out = logits;
+  S.out = part;
   S.ldo = p->E;
   S.rows = p->T;
   S.m_slots = (p->T + pl.bm - 1) / pl.bm;
+  S.ksplit = splits;
+  S.split_stride = static_cast<int64_t>(p->T) * p->E;
   finish_grid(g, pl, false);
   return run_gemm(g, pl, false, p->act_dtype, p->act_dtype, MOE_F32, s);
 }
@@ -253,11 +287,12 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_rout
   if (p->T == 0) return MOE_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (!logits_given) {
+    // no workspace here: the router writes whole sums straight into `logits`
     StageScope sc(ST_ROUTER, s);
-    MOE_LAUNCH(launch_router(p, x, w_router, logits, s));
+    MOE_LAUNCH(launch_router(p, x, w_router, logits, 1, s));
   }
   StageScope sc(ST_TOPK, s);
-  MOE_LAUNCH(launch_topk_softmax(logits, p->T, p->E, p->k, topk_idx, topk_w, s));
+  MOE_LAUNCH(launch_topk_softmax(logits, 1, nullptr, p->T, p->E, p->k, topk_idx, topk_w, s));
   return MOE_OK;
 }
 
@@ -323,8 +358,8 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t r
   const bool fp8 = p->w_dtype == MOE_FP8_E4M3FN;
   {
     StageScope sc(ST_TILES, s);
-    MOE_LAUNCH(launch_build_tiles(offsets, n_groups, pl.bm, rows_upper_bound, tile_ub, tiles,
-                                  ntiles, s));
+    MOE_LAUNCH(launch_build_tiles(offsets, n_groups, pl.bm, rows_upper_bound, tile_ub, pl.tiled,
+                                  tiles, ntiles, s));
   }
   GArgs g1{};
   g1.nsets = 1;
@@ -423,7 +458,11 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     using Ptr = decltype(user);
     return user ? user : reinterpret_cast<Ptr>(w + off);
   };
-  float* logits = A->logits_in ? const_cast<float*>(A->logits_in) : pick(A->logits_out, L.logits);
+  // router partial sums (or whole logits when not split), then top-k
+  float* part = A->logits_in ? const_cast<float*>(A->logits_in)
+                : (L.splits == 1 ? pick(A->logits_out, L.logits) : reinterpret_cast<float*>(w + L.logits));
+  const int splits = A->logits_in ? 1 : L.splits;
+  float* logits_write = (A->logits_out && part != A->logits_out) ? A->logits_out : nullptr;
   int32_t* idx = pick(A->topk_idx_out, L.idx);
   float* tw = pick(A->topk_w_out, L.w);
   int32_t* counts = pick(A->counts_out, L.counts);
@@ -442,11 +481,11 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
   // 1. router logits (fp32) and top-k softmax
   if (!A->logits_in) {
     StageScope sc(ST_ROUTER, s);
-    MOE_LAUNCH(launch_router(p, A->x, A->w_router, logits, s));
+    MOE_LAUNCH(launch_router(p, A->x, A->w_router, part, L.splits, s));
   }
   {
     StageScope sc(ST_TOPK, s);
-    MOE_LAUNCH(launch_topk_softmax(logits, p->T, p->E, p->k, idx, tw, s));
+    MOE_LAUNCH(launch_topk_softmax(part, splits, logits_write, p->T, p->E, p->k, idx, tw, s));
   }
   // 2. permutation and the M-tile table
   {
@@ -457,8 +496,8 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
   }
   {
     StageScope sc(ST_TILES, s);
-    MOE_LAUNCH(launch_build_tiles(offsets, p->E, pl.bm, static_cast<int>(Tk), L.tile_ub, tiles,
-                                  ntiles, s));
+    MOE_LAUNCH(launch_build_tiles(offsets, p->E, pl.bm, static_cast<int>(Tk), L.tile_ub, pl.tiled,
+                                  tiles, ntiles, s));
   }
   // 3. grouped FFN: shared branch (dense rows) and routed experts in the same launches
   const bool fp8 = p->w_dtype == MOE_FP8_E4M3FN;

@@ -32,6 +32,26 @@ namespace {
 constexpr int NF = 4;            // 16-row weight fragments per wavefront
 constexpr int WAVES = 4;         // wavefronts per block (consecutive N tiles)
 
+// Build-time tuning knobs (defaults are the measured choice):
+//   MOE_STREAM_NT  1: weight loads carry the non-temporal hint (read once)
+//   MOE_STREAM_U1  K-steps per register stage when tiles are one 16-row chunk
+#ifndef MOE_STREAM_NT
+#define MOE_STREAM_NT 0
+#endif
+#ifndef MOE_STREAM_U1
+#define MOE_STREAM_U1 4
+#endif
+
+__device__ __forceinline__ uint4 load_w(const uint4* p) {
+#if MOE_STREAM_NT
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return uint4{v[0], v[1], v[2], v[3]};
+#else
+  return *p;
+#endif
+}
+
 template <int DT> struct Elt;
 template <> struct Elt<DT_F32> { static constexpr int bytes = 4; };
 template <> struct Elt<DT_BF16> { static constexpr int bytes = 2; };
@@ -41,58 +61,6 @@ template <> struct Elt<DT_FP8> { static constexpr int bytes = 1; };
 template <int DT, int U> struct VecCount {
   static constexpr int n = (8 * U * Elt<DT>::bytes) / 16;
 };
-
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(lo), 1.0f, false);
-  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(lo), 1.0f, true);
-  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(hi), 1.0f, false);
-  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(hi), 1.0f, true);
-  bf16x8 r;
-  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-  return r;
-}
-
-// Operand of one MFMA step (8 K-elements per lane) from the staged uint4s.
-template <int DT>
-__device__ __forceinline__ bf16x8 operand_bf16(const uint4* v, int u) {
-  if constexpr (DT == DT_BF16) {
-    return __builtin_bit_cast(bf16x8, v[u]);
-  } else {  // DT_FP8: 8 bytes of step u
-    const uint4 q = v[u >> 1];
-    return (u & 1) ? fp8x8_to_bf16x8(q.z, q.w) : fp8x8_to_bf16x8(q.x, q.y);
-  }
-}
-
-__device__ __forceinline__ float act_fn(int act, float z) {
-  if (act == ACT_SILU) return z / (1.0f + expf(-z));
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
-}
-
-// Which set / M-tile / N-block a block works on; false if it has no work.
-__device__ __forceinline__ bool resolve_block(const GArgs& g, int b, int& si, int& group, int& row0,
-                                              int& row1, int& nblk) {
-  si = (g.nsets > 1 && b >= g.s[1].block0) ? 1 : 0;
-  const GSet& S = g.s[si];
-  const int local = b - S.block0;
-  const int m = local / S.blocks_per_m;
-  nblk = local - m * S.blocks_per_m;
-  if (S.tiles) {
-    if (m >= S.n_tiles[0]) return false;
-    const GTile t = S.tiles[m];
-    group = t.group;
-    row0 = t.row0;
-    row1 = t.row1;
-  } else {
-    row0 = m * S.bm;
-    if (row0 >= S.rows) return false;
-    row1 = min(row0 + S.bm, S.rows);
-    group = 0;
-  }
-  return row1 > row0;
-}
 
 template <int MT, int U, bool GATED, int ADT, int WDT, int ODT>
 __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs g) {
@@ -110,6 +78,10 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
   if (wn >= waves_n) return;
   const int K = S.K;
   const int nch = (row1 - row0 + 15) >> 4;  // active 16-row chunks (<= MT)
+  // K slice of this block (plain fp32 outputs may be split into partial sums)
+  const int split = S.ksplit > 1 ? static_cast<int>((blockIdx.x - S.block0) % S.ksplit) : 0;
+  const int k_len = S.ksplit > 1 ? K / S.ksplit : K;
+  const int k_beg = split * k_len;
 
   // ---- operand pointers (element offsets are per lane: row + q*8U)
   const char* a_base = static_cast<const char*>(S.a);
@@ -127,7 +99,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
         arow = 0;
       }
     }
-    ap[mc] = a_base + (arow * S.lda + q * 8 * U) * Elt<ADT>::bytes;
+    ap[mc] = a_base + (arow * S.lda + k_beg + q * 8 * U) * Elt<ADT>::bytes;
   }
   const char* w_base = static_cast<const char*>(S.w) + group * S.w_gstride * Elt<WDT>::bytes;
   const char* bp[NF];
@@ -143,7 +115,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
       bv[f] = n < n_out;
       if (!bv[f]) n = 0;
     }
-    bp[f] = w_base + (static_cast<int64_t>(n) * K + q * 8 * U) * Elt<WDT>::bytes;
+    bp[f] = w_base + (static_cast<int64_t>(n) * K + k_beg + q * 8 * U) * Elt<WDT>::bytes;
   }
 
   f32x4 acc[MT][NF];
@@ -160,7 +132,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
     for (int f = 0; f < NF; ++f) {
       const uint4* p = reinterpret_cast<const uint4*>(bp[f] + koff * Elt<WDT>::bytes);
 #pragma unroll
-      for (int v = 0; v < BV; ++v) sb[f][v] = bv[f] ? p[v] : uint4{0, 0, 0, 0};
+      for (int v = 0; v < BV; ++v) sb[f][v] = bv[f] ? load_w(p + v) : uint4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int mc = 0; mc < MT; ++mc) {
@@ -206,7 +178,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
     }
   };
 
-  const int nst = K / KS;
+  const int nst = k_len / KS;
   load(sa0, sb0, 0);
   for (int st = 0; st < nst; st += 2) {
     if (st + 1 < nst) load(sa1, sb1, st + 1);
@@ -219,7 +191,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
 
   // ---- epilogue: C[row = 4*q + j][col = lr] of each 16x16 fragment
   const float* sc = S.scale ? S.scale + group * S.s_gstride : nullptr;
-  char* out = static_cast<char*>(S.out);
+  char* out = static_cast<char*>(S.out) + split * S.split_stride * Elt<ODT>::bytes;
 #pragma unroll
   for (int mc = 0; mc < MT; ++mc) {
     if (mc >= nch) continue;
@@ -267,9 +239,10 @@ template <int MT, bool GATED, int ADT, int WDT, int ODT>
 hipError_t pick_u(const GArgs& g, hipStream_t s) {
   // four-step stages when every K allows and registers do (bf16/fp8 operands,
   // at most two 16-row chunks); fp32 operands always use two-step stages
-  if constexpr (MT <= 2 && ADT != DT_F32) {
+  if constexpr (MT <= 2 && ADT != DT_F32 && !(MT == 1 && MOE_STREAM_U1 == 2)) {
     bool k128 = true;
-    for (int i = 0; i < g.nsets; ++i) k128 = k128 && g.s[i].K % 128 == 0;
+    for (int i = 0; i < g.nsets; ++i)
+      k128 = k128 && (g.s[i].K / (g.s[i].ksplit > 1 ? g.s[i].ksplit : 1)) % 128 == 0;
     if (k128) return launch_one<MT, 4, GATED, ADT, WDT, ODT>(g, s);
   }
   return launch_one<MT, 2, GATED, ADT, WDT, ODT>(g, s);

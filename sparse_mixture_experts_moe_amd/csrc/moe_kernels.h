@@ -56,7 +56,8 @@ struct GSet {
   int32_t block0;           // first block id of this set
   int32_t blocks_per_m;     // blocks per m-tile slot (N direction)
   int32_t bm;               // rows per m-tile
-  int32_t pad1;
+  int32_t ksplit;           // K slices (>1 only for plain fp32 outputs: partial sums)
+  int64_t split_stride;     // output elements between the partial sums of two slices
 };
 
 struct GArgs {
@@ -65,12 +66,70 @@ struct GArgs {
   int32_t total_blocks;
 };
 
+// ------------------------------------------------------------------ device helpers
+// fp8 e4m3fn -> bf16 is exact (every e4m3fn value is a bf16 value):
+// v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two codes per instruction.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(lo), 1.0f, false);
+  const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(lo), 1.0f, true);
+  const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(hi), 1.0f, false);
+  const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(static_cast<int>(hi), 1.0f, true);
+  bf16x8 r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Operand of one MFMA step (8 K-elements per lane) from staged uint4s.
+template <int DT>
+__device__ __forceinline__ bf16x8 operand_bf16(const uint4* v, int u) {
+  if constexpr (DT == DT_BF16) {
+    return __builtin_bit_cast(bf16x8, v[u]);
+  } else {  // DT_FP8: 8 bytes of step u
+    const uint4 q = v[u >> 1];
+    return (u & 1) ? fp8x8_to_bf16x8(q.z, q.w) : fp8x8_to_bf16x8(q.x, q.y);
+  }
+}
+
+__device__ __forceinline__ float act_fn(int act, float z) {
+  if (act == ACT_SILU) return z / (1.0f + expf(-z));
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * z * (1.0f + tanhf(c * (z + 0.044715f * z * z * z)));
+}
+
+// Which set / M-tile / N-block a block works on; false if it has no work.
+__device__ __forceinline__ bool resolve_block(const GArgs& g, int b, int& si, int& group, int& row0,
+                                              int& row1, int& nblk) {
+  si = (g.nsets > 1 && b >= g.s[1].block0) ? 1 : 0;
+  const GSet& S = g.s[si];
+  int local = b - S.block0;
+  if (S.ksplit > 1) local /= S.ksplit;
+  const int m = local / S.blocks_per_m;
+  nblk = local - m * S.blocks_per_m;
+  if (S.tiles) {
+    if (m >= S.n_tiles[0]) return false;
+    const GTile t = S.tiles[m];
+    group = t.group;
+    row0 = t.row0;
+    row1 = t.row1;
+  } else {
+    row0 = m * S.bm;
+    if (row0 >= S.rows) return false;
+    row1 = min(row0 + S.bm, S.rows);
+    group = 0;
+  }
+  return row1 > row0;
+}
+
 // ------------------------------------------------------------------ launchers
 // Each returns hipSuccess or the launch error.
 
-// logits[T,E] (fp32) -> topk idx / weights.
-hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx,
-                               float* w, hipStream_t s);
+// Router logits given as `splits` partial sums part[s][T][E] (fp32), added in
+// slice order -> topk idx / weights; the summed logits are written to
+// logits_out when it is not null.
+hipError_t launch_topk_softmax(const float* part, int splits, float* logits_out, int T, int E,
+                               int k, int32_t* idx, float* w, hipStream_t s);
 
 // Permutation: per-block bit masks -> counts/offsets -> stable scatter.
 int perm_blocks(int T);
@@ -78,10 +137,12 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* blk 
                           int32_t* local_rank /*[T*k]*/, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* row_of_slot, hipStream_t s);
 
-// M-tile table of n_groups groups from device offsets (largest group first).
-// Offsets are clamped to [0, max_rows] and at most max_tiles entries are written.
+// M-tile table of n_groups groups from device offsets, in group order or, with
+// largest_first, by descending group size (ties by group id).  Offsets are
+// clamped to [0, max_rows] and at most max_tiles entries are written.
 hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int bm, int max_rows,
-                              int max_tiles, GTile* tiles, int32_t* n_tiles, hipStream_t s);
+                              int max_tiles, bool largest_first, GTile* tiles, int32_t* n_tiles,
+                              hipStream_t s);
 
 // Grouped GEMM, streamed weights.  mt = 16-row chunks per m-tile (1, 2, 4).
 // gated: h = act(A.Wg^T * sg) * (A.Wu^T * su); plain: out = A.W^T * s.

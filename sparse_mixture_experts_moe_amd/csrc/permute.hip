@@ -109,38 +109,45 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
   row_of_slot[a] = r;
 }
 
-// Single block: each group's M-tiles, groups ordered by descending row count
-// (ties by group id) so the heaviest experts start first.
+// Single block: each group's M-tiles.  With largest_first the groups are
+// ordered by descending row count (ties by group id) so the heaviest experts
+// start first; otherwise in group order.
 constexpr int TILE_THREADS = 1024;
 
 __device__ __forceinline__ int clamp_row(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 __global__ __launch_bounds__(TILE_THREADS) void build_tiles_kernel(const int32_t* __restrict__ offsets,
                                                                    int G, int bm, int max_rows,
-                                                                   int max_tiles,
+                                                                   int max_tiles, int largest_first,
                                                                    GTile* __restrict__ tiles,
                                                                    int32_t* __restrict__ n_tiles) {
+  __shared__ int32_t sz[TILE_THREADS];    // group sizes (offsets clamped to [0, max_rows])
   __shared__ int32_t ntl[TILE_THREADS];   // tiles of the group at each rank position
   __shared__ int32_t grp[TILE_THREADS];   // group at each rank position
   const int g = threadIdx.x;
-  int n = 0, rank = 0;
-  // group sizes from offsets clamped to [0, max_rows] (non-decreasing)
-  auto lo = [&](int i) { return clamp_row(offsets[i], 0, max_rows); };
-  auto size = [&](int i) { const int a = lo(i); return clamp_row(offsets[i + 1], a, max_rows) - a; };
+  int r0 = 0, n = 0;
   if (g < G) {
-    n = size(g);
+    r0 = clamp_row(offsets[g], 0, max_rows);
+    n = clamp_row(offsets[g + 1], r0, max_rows) - r0;
+  }
+  sz[g] = n;
+  __syncthreads();
+  int rank = g;
+  if (largest_first && g < G) {
+    rank = 0;
     for (int o = 0; o < G; ++o) {
-      const int no = size(o);
+      const int no = sz[o];
       rank += (no > n) || (no == n && o < g);
     }
   }
+  ntl[g] = 0;
+  __syncthreads();
   if (g < G) {
     ntl[rank] = (n + bm - 1) / bm;
     grp[rank] = g;
   }
-  for (int i = G + threadIdx.x; i < TILE_THREADS; i += TILE_THREADS) ntl[i] = 0;
   __syncthreads();
-  // inclusive scan of tiles in rank order
+  // inclusive scan of tile counts in rank order
   for (int off = 1; off < TILE_THREADS; off <<= 1) {
     const int add = g >= off ? ntl[g - off] : 0;
     __syncthreads();
@@ -149,13 +156,14 @@ __global__ __launch_bounds__(TILE_THREADS) void build_tiles_kernel(const int32_t
   }
   if (g < G) {
     const int gg = grp[g];
-    const int r0 = lo(gg), r1 = r0 + size(gg);
+    const int a = clamp_row(offsets[gg], 0, max_rows);
+    const int b = a + sz[gg];
     const int base = g > 0 ? ntl[g - 1] : 0;
-    for (int i = 0, r = r0; r < r1 && base + i < max_tiles; ++i, r += bm) {
+    for (int i = 0, r = a; r < b && base + i < max_tiles; ++i, r += bm) {
       GTile tl;
       tl.group = gg;
       tl.row0 = r;
-      tl.row1 = r + bm < r1 ? r + bm : r1;
+      tl.row1 = r + bm < b ? r + bm : b;
       tl.pad = 0;
       tiles[base + i] = tl;
     }
@@ -188,9 +196,10 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* blk,
 }
 
 hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int bm, int max_rows,
-                              int max_tiles, GTile* tiles, int32_t* n_tiles, hipStream_t s) {
-  build_tiles_kernel<<<1, TILE_THREADS, 0, s>>>(offsets, n_groups, bm, max_rows, max_tiles, tiles,
-                                                n_tiles);
+                              int max_tiles, bool largest_first, GTile* tiles, int32_t* n_tiles,
+                              hipStream_t s) {
+  build_tiles_kernel<<<1, TILE_THREADS, 0, s>>>(offsets, n_groups, bm, max_rows, max_tiles,
+                                                largest_first ? 1 : 0, tiles, n_tiles);
   return hipGetLastError();
 }
 

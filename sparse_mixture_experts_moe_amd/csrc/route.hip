@@ -18,19 +18,36 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+// The router product may arrive as `splits` partial sums (a K-split GEMM);
+// they are added here in slice order, so the logits are deterministic.
 template <int EPL>
 __global__ __launch_bounds__(64 * WAVES_PER_BLOCK) void topk_softmax_kernel(
-    const float* __restrict__ logits, int T, int E, int k, int32_t* __restrict__ idx,
-    float* __restrict__ wout) {
+    const float* __restrict__ part, int splits, float* __restrict__ logits_out, int T, int E,
+    int k, int32_t* __restrict__ idx, float* __restrict__ wout) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * WAVES_PER_BLOCK + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + static_cast<int64_t>(t) * E;
+  const int64_t slice = static_cast<int64_t>(T) * E;
+  const float* row = part + static_cast<int64_t>(t) * E;
   float v[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    v[j] = e < E ? row[e] : -__builtin_inff();
+    float l = -__builtin_inff();
+    if (e < E) {
+      // load up to 8 slices at a time, then add them in slice order
+      l = row[e];
+      for (int s0 = 1; s0 < splits; s0 += 8) {
+        float pv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pv[u] = s0 + u < splits ? row[(s0 + u) * slice + e] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < splits) l += pv[u];
+      }
+      if (logits_out) logits_out[static_cast<int64_t>(t) * E + e] = l;
+    }
+    v[j] = l;
   }
   uint32_t taken = 0;
   float my_v = 0.f, top_v = 0.f;
@@ -75,21 +92,21 @@ __global__ __launch_bounds__(64 * WAVES_PER_BLOCK) void topk_softmax_kernel(
 
 }  // namespace
 
-hipError_t launch_topk_softmax(const float* logits, int T, int E, int k, int32_t* idx, float* w,
-                               hipStream_t s) {
+hipError_t launch_topk_softmax(const float* part, int splits, float* logits_out, int T, int E,
+                               int k, int32_t* idx, float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const dim3 grid((T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK), block(64 * WAVES_PER_BLOCK);
   const int epl = (E + 63) / 64;
   if (epl <= 1)
-    topk_softmax_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+    topk_softmax_kernel<1><<<grid, block, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
   else if (epl <= 2)
-    topk_softmax_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+    topk_softmax_kernel<2><<<grid, block, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
   else if (epl <= 4)
-    topk_softmax_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+    topk_softmax_kernel<4><<<grid, block, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
   else if (epl <= 8)
-    topk_softmax_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+    topk_softmax_kernel<8><<<grid, block, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
   else
-    topk_softmax_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, idx, w);
+    topk_softmax_kernel<16><<<grid, block, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
   return hipGetLastError();
 }
 
