@@ -59,14 +59,15 @@ constexpr bool kTiledReady = true;
 // Largest mean rows per group for which the streamed GEMM uses 32-row tiles
 // (build-time tuning knob).
 #ifndef MOE_MT2_MEAN
-#define MOE_MT2_MEAN 12.0
+#define MOE_MT2_MEAN 24.0
 #endif
+
 
 Plan make_plan(const moe_problem_t* p, double mean_rows) {
   const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16;
   int policy = p->tile_policy;
   if (policy == MOE_TILE_AUTO) policy = (tiled_ok && mean_rows > 48.0) ? MOE_TILE_LDS : MOE_TILE_STREAM;
-  if (policy == MOE_TILE_LDS && tiled_ok) return Plan{true, 0, tiled_bm()};
+  if (policy == MOE_TILE_LDS && tiled_ok) return Plan{true, 0, 128};
   int mt = mean_rows <= 4.0 ? 1 : mean_rows <= MOE_MT2_MEAN ? 2 : 4;
   mt = std::min(mt, stream_max_mt(p->act_dtype));
   return Plan{false, mt, 16 * mt};
@@ -99,7 +100,7 @@ void finish_grid(GArgs& g, const Plan& pl, bool gated) {
 // stream the router weight.
 Plan router_plan(const moe_problem_t* p) {
   if (kTiledReady && p->act_dtype == MOE_BF16 && p->T >= 1024 && p->tile_policy != MOE_TILE_STREAM)
-    return Plan{true, 0, tiled_bm()};
+    return Plan{true, 0, 128};
   int mt = p->T <= 16 ? 1 : p->T <= 32 ? 2 : 4;
   mt = std::min(mt, stream_max_mt(p->act_dtype));
   return Plan{false, mt, 16 * mt};
@@ -119,7 +120,7 @@ int router_splits(const moe_problem_t* p, const Plan& pl) {
 
 hipError_t run_gemm(const GArgs& g, const Plan& pl, bool gated, int a_dt, int w_dt, int o_dt,
                     hipStream_t s) {
-  if (pl.tiled) return launch_tiled_gemm(g, gated, w_dt, o_dt, s);
+  if (pl.tiled) return launch_tiled_gemm(g, pl.bm, gated, w_dt, o_dt, s);
   return launch_stream_gemm(g, pl.mt, gated, a_dt, w_dt, o_dt, s);
 }
 

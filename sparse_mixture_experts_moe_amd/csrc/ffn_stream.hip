@@ -39,7 +39,7 @@ constexpr int WAVES = 4;         // wavefronts per block (consecutive N tiles)
 #define MOE_STREAM_NT 0
 #endif
 #ifndef MOE_STREAM_U1
-#define MOE_STREAM_U1 4
+#define MOE_STREAM_U1 2
 #endif
 
 __device__ __forceinline__ uint4 load_w(const uint4* p) {
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
 
   uint4 sa0[MT][AV], sb0[NF][BV], sa1[MT][AV], sb1[NF][BV];
 
-  auto load = [&](uint4 (&sa)[MT][AV], uint4 (&sb)[NF][BV], int stage) {
+  auto load = [&](uint4 (&sa)[MT][AV], uint4 (&sb)[NF][BV], int stage) __attribute__((always_inline)) {
     const int64_t koff = static_cast<int64_t>(stage) * KS;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
     }
   };
 
-  auto compute = [&](const uint4 (&sa)[MT][AV], const uint4 (&sb)[NF][BV]) {
+  auto compute = [&](const uint4 (&sa)[MT][AV], const uint4 (&sb)[NF][BV]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if constexpr (ADT == DT_F32) {

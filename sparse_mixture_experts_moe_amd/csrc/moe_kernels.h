@@ -12,6 +12,7 @@ enum : int { ACT_SILU = 0, ACT_GELU_TANH = 1 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // 16 raw bytes in registers
 
 // bf16 storage is handled as raw uint16_t.
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
@@ -152,10 +153,10 @@ hipError_t launch_stream_gemm(const GArgs& g, int mt, bool gated, int a_dtype, i
 int stream_waves_n(bool gated, int n_out);   // wave tiles along N per m-tile
 int stream_max_mt(int a_dtype);              // largest mt the stream kernel runs for a dtype
 
-// Grouped GEMM, LDS-tiled (bf16 activations, bf16 or fp8 weights).
-hipError_t launch_tiled_gemm(const GArgs& g, bool gated, int w_dtype, int out_dtype,
+// Grouped GEMM, LDS-tiled (bf16 activations, bf16 or fp8 weights); bm = 128 or
+// 256 rows per M-tile (every set's bm must match).
+hipError_t launch_tiled_gemm(const GArgs& g, int bm, bool gated, int w_dtype, int out_dtype,
                              hipStream_t s);
-int tiled_bm();
 int tiled_blocks_n(bool gated, int n_out);
 
 // Decode n (multiple of 8) fp8 e4m3fn codes to bf16 with the GEMM's own decoder.

@@ -22,6 +22,10 @@ SMALL = {
     "gemma_like": shrink(CONFIGS["gemma"], T=200, D=320, E=16, k=8, I=192, I_shared=320),
     "ling_fp8": shrink(CONFIGS["ling_decode"], T=130, D=256, E=16, k=8, I=128, I_shared=128),
     "fp32_ragged": shrink(CONFIGS["tiny_fp32"], T=77, D=192, E=12, k=3, I=64),
+    # more than 256 rows per expert on average: 256-row LDS tiles with ragged tails
+    "big_groups_bf16": shrink(CONFIGS["qwen_prefill"], T=1100, D=256, E=4, k=2, I=192, I_shared=128,
+                              zipf=False),
+    "big_groups_fp8": shrink(CONFIGS["ling_prefill"], T=1030, D=320, E=4, k=2, I=128, I_shared=192),
 }
 
 
@@ -76,7 +80,10 @@ def test_layer_small_on_device_logits(name):
     same = np.all(np.sort(res["topk_idx"].cpu().numpy(), 1) == np.sort(ref["idx"], 1), axis=1)
     assert same.mean() >= 0.99
     if same.all():
-        _check_routing(res, ref)
+        # the weights come from the device's own logits, which differ from the
+        # oracle's by rounding: |dw/w| <= 2 max|dl| (softmax over the top-k)
+        dl = float(np.max(np.abs(lg - lr)))
+        _check_routing(res, ref, w_rtol=1e-6 + 2.5 * dl)
         assert rel_err(f64(res["y"]), ref["y"]) <= tol_for(cfg)
     else:
         assert rel_err(f64(res["y"])[same], ref["y"][same]) <= tol_for(cfg)
