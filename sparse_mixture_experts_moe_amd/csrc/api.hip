@@ -318,9 +318,14 @@ moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_
   char* w = static_cast<char*>(ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   StageScope sc(ST_PERMUTE, s);
-  MOE_LAUNCH(launch_permute(topk_idx, p->T, p->k, p->E, reinterpret_cast<int32_t*>(w + L.blk),
-                            reinterpret_cast<int32_t*>(w + L.rank), counts, offsets, row_token,
-                            row_of_slot, s));
+  if (p->T <= perm_small_max_tokens()) {
+    MOE_LAUNCH(launch_permute_small(topk_idx, p->T, p->k, p->E, counts, offsets, row_token,
+                                    row_of_slot, 1, 0, nullptr, nullptr, s));
+  } else {
+    MOE_LAUNCH(launch_permute(topk_idx, p->T, p->k, p->E, reinterpret_cast<int32_t*>(w + L.blk),
+                              reinterpret_cast<int32_t*>(w + L.rank), counts, offsets, row_token,
+                              row_of_slot, s));
+  }
   return MOE_OK;
 }
 
@@ -488,17 +493,23 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     StageScope sc(ST_TOPK, s);
     MOE_LAUNCH(launch_topk_softmax(part, splits, logits_write, p->T, p->E, p->k, idx, tw, s));
   }
-  // 2. permutation and the M-tile table
-  {
+  // 2. permutation and the M-tile table (one launch for small batches)
+  if (p->T <= perm_small_max_tokens() && !pl.tiled) {
     StageScope sc(ST_PERMUTE, s);
-    MOE_LAUNCH(launch_permute(idx, p->T, p->k, p->E, reinterpret_cast<int32_t*>(w + L.blk),
-                              reinterpret_cast<int32_t*>(w + L.rank), counts, offsets, row_token,
-                              row_of_slot, s));
-  }
-  {
-    StageScope sc(ST_TILES, s);
-    MOE_LAUNCH(launch_build_tiles(offsets, p->E, pl.bm, static_cast<int>(Tk), L.tile_ub, pl.tiled,
-                                  tiles, ntiles, s));
+    MOE_LAUNCH(launch_permute_small(idx, p->T, p->k, p->E, counts, offsets, row_token, row_of_slot,
+                                    pl.bm, L.tile_ub, tiles, ntiles, s));
+  } else {
+    {
+      StageScope sc(ST_PERMUTE, s);
+      MOE_LAUNCH(launch_permute(idx, p->T, p->k, p->E, reinterpret_cast<int32_t*>(w + L.blk),
+                                reinterpret_cast<int32_t*>(w + L.rank), counts, offsets, row_token,
+                                row_of_slot, s));
+    }
+    {
+      StageScope sc(ST_TILES, s);
+      MOE_LAUNCH(launch_build_tiles(offsets, p->E, pl.bm, static_cast<int>(Tk), L.tile_ub, pl.tiled,
+                                    tiles, ntiles, s));
+    }
   }
   // 3. grouped FFN: shared branch (dense rows) and routed experts in the same launches
   const bool fp8 = p->w_dtype == MOE_FP8_E4M3FN;

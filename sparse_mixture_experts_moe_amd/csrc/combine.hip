@@ -2,15 +2,17 @@
 //   y[t] = sum_{j<k} w[t,j] * o_perm[row_of_slot[t*k+j]] + shared[t]
 // ("finalize routing" on the "CANN Qwen3-MoE" page; the unpermute and local
 // reduce of the "Qwen 3.5 MoE on Ironwood" page's MoE track, which reads each
-// expert output row once and writes each token row once).  One block per token
-// row; every thread owns 8 consecutive hidden elements (16-byte accesses in
-// bf16), accumulates in fp32 in slot order and rounds once.
+// expert output row once and writes each token row once).  One block per (token
+// row, 1024-column chunk), so a small batch still spreads over the whole GPU;
+// every thread owns 8 consecutive hidden elements (16-byte accesses in bf16),
+// accumulates in fp32 in slot order and rounds once.
 #include "moe_kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int THREADS = 256;
+constexpr int THREADS = 128;
+constexpr int CHUNK = THREADS * 8;   // hidden elements per block
 constexpr int MAXK = 32;
 
 template <int DT>
@@ -61,7 +63,9 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const void* __restrict
     ws[threadIdx.x] = w[static_cast<int64_t>(t) * k + threadIdx.x];
   }
   __syncthreads();
-  for (int d = threadIdx.x * 8; d < D; d += THREADS * 8) {
+  {
+    const int d = blockIdx.y * CHUNK + threadIdx.x * 8;
+    if (d >= D) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j = 0; j < k; ++j) {
       const int r = rows[j];
@@ -88,10 +92,11 @@ hipError_t launch_combine(const void* o_perm, const int32_t* row_of_slot, const 
                           const void* shared, int T, int D, int k, int dtype, void* y,
                           hipStream_t s) {
   if (T == 0) return hipSuccess;
+  const dim3 grid(T, (D + CHUNK - 1) / CHUNK);
   if (dtype == DT_BF16)
-    combine_kernel<DT_BF16><<<T, THREADS, 0, s>>>(o_perm, row_of_slot, w, shared, D, k, y);
+    combine_kernel<DT_BF16><<<grid, THREADS, 0, s>>>(o_perm, row_of_slot, w, shared, D, k, y);
   else
-    combine_kernel<DT_F32><<<T, THREADS, 0, s>>>(o_perm, row_of_slot, w, shared, D, k, y);
+    combine_kernel<DT_F32><<<grid, THREADS, 0, s>>>(o_perm, row_of_slot, w, shared, D, k, y);
   return hipGetLastError();
 }
 

@@ -21,8 +21,10 @@
 //
 // LDS rows hold 32 bf16 (64 bytes, 4 chunks of 16); chunk c of row r sits at
 // c ^ ((r >> 1) & 3), which keeps the 16-byte copy stores and fragment reads
-// free of bank conflicts.  fp8 e4m3fn weights are decoded exactly to bf16 on
-// the way into LDS; per-channel scales are applied after the reduction.
+// free of bank conflicts.  fp8 e4m3fn weights stay fp8 in LDS (32-byte rows of
+// four 8-byte chunks, chunk c of row r at c ^ ((r >> 2) & 3)) and are decoded
+// exactly to bf16 as fragments are read, which halves the weight tile's LDS
+// traffic; per-channel scales are applied after the reduction.
 //
 // Blocks are remapped so that consecutive tiles (the M-tiles and N-blocks of
 // one expert) run on the same XCD and share its L2; the remap spans only the
@@ -41,12 +43,13 @@ constexpr int BNW = 256;                  // weight rows per block
 constexpr int BK = 32;                    // K elements per stage
 constexpr int NSTAGE = 2;                 // LDS buffers
 constexpr int THREADS = 256;
-constexpr int ROWB = BK * 2;              // LDS bytes per tile row (64)
-constexpr int B_BYTES = BNW * ROWB;       // 16 KiB
+constexpr int ROWB = BK * 2;              // LDS bytes per bf16 tile row (64)
+constexpr int ROWB8 = BK;                 // LDS bytes per fp8 tile row (32)
 constexpr int NXCD = 8;
 
-template <int BM> struct Cfg {
+template <int BM, bool FP8> struct Cfg {
   static constexpr int A_BYTES = BM * ROWB;
+  static constexpr int B_BYTES = BNW * (FP8 ? ROWB8 : ROWB);
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int WM = BM / 2;           // rows per wavefront
   static constexpr int TF = WM / 16;          // row (token) fragments per wavefront
@@ -57,7 +60,11 @@ template <int BM> struct Cfg {
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * ROWB + ((chunk ^ ((row >> 1) & 3)) << 4);
 }
+__device__ __forceinline__ int swz8(int row, int chunk) {
+  return row * ROWB8 + ((chunk ^ ((row >> 2) & 3)) << 3);
+}
 
+#if MOE_TILED_REMAP
 // Logical tile of a physical block: consecutive logical tiles share an XCD.
 __device__ __forceinline__ bool remap_block(const GArgs& g, int& logical) {
   int real = 0;
@@ -86,10 +93,11 @@ __device__ __forceinline__ bool remap_block(const GArgs& g, int& logical) {
   }
   return false;
 }
+#endif
 
 template <int BM, bool GATED, int WDT, int ODT>
 __global__ __launch_bounds__(THREADS, 2) void tiled_gemm_kernel(const GArgs g) {
-  using C = Cfg<BM>;
+  using C = Cfg<BM, WDT == DT_FP8>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   // An (empty) statement that names an accumulation register makes the backend
   // select the AGPR form of the MFMAs, so the accumulators live in AGPRs and
@@ -174,8 +182,8 @@ __global__ __launch_bounds__(THREADS, 2) void tiled_gemm_kernel(const GArgs g) {
       const int tr = brow0 + BSTEP * i;
       if constexpr (FP8) {
         const u32x4 v = rb[i];
-        *reinterpret_cast<bf16x8*>(bb + swz(tr, 2 * bcol)) = fp8x8_to_bf16x8(v[0], v[1]);
-        *reinterpret_cast<bf16x8*>(bb + swz(tr, 2 * bcol + 1)) = fp8x8_to_bf16x8(v[2], v[3]);
+        *reinterpret_cast<uint2*>(bb + swz8(tr, 2 * bcol)) = uint2{v[0], v[1]};
+        *reinterpret_cast<uint2*>(bb + swz8(tr, 2 * bcol + 1)) = uint2{v[2], v[3]};
       } else {
         *reinterpret_cast<u32x4*>(bb + swz(tr, cc)) = rb[i];
       }
@@ -197,7 +205,12 @@ __global__ __launch_bounds__(THREADS, 2) void tiled_gemm_kernel(const GArgs g) {
     for (int f = 0; f < 8; ++f) {
       const int tr = GATED ? ((f < 4 ? 0 : BNW / 2) + wn * 64 + (f & 3) * 16 + lr)
                            : (wn * 128 + f * 16 + lr);
-      wf[f] = *reinterpret_cast<const bf16x8*>(bb + swz(tr, q));
+      if constexpr (WDT == DT_FP8) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(bb + swz8(tr, q));
+        wf[f] = fp8x8_to_bf16x8(raw.x, raw.y);
+      } else {
+        wf[f] = *reinterpret_cast<const bf16x8*>(bb + swz(tr, q));
+      }
     }
 #pragma unroll
     for (int i = 0; i < C::TF; ++i)

@@ -174,9 +174,98 @@ __global__ __launch_bounds__(TILE_THREADS) void build_tiles_kernel(const int32_t
   }
 }
 
+// Batches of at most PB tokens (decode): the whole permutation and the M-tile
+// table (in group order) in one block, with the same bit-mask ranking.
+__device__ __forceinline__ int block_inclusive_scan(int32_t* sc, int v) {
+  const int i = threadIdx.x;
+  sc[i] = v;
+  __syncthreads();
+  for (int off = 1; off < SCAN_THREADS; off <<= 1) {
+    const int add = i >= off ? sc[i - off] : 0;
+    __syncthreads();
+    sc[i] += add;
+    __syncthreads();
+  }
+  return sc[i];
+}
+
+__global__ __launch_bounds__(SCAN_THREADS) void perm_small_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ row_of_slot,
+    int bm, int max_tiles, GTile* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  __shared__ unsigned long long mask[SCAN_THREADS * WORDS];   // [E][WORDS]
+  __shared__ int32_t sc[SCAN_THREADS];
+  __shared__ int32_t off_s[SCAN_THREADS + 1];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * WORDS; i += SCAN_THREADS) mask[i] = 0ull;
+  __syncthreads();
+  const int n = T * k;
+  for (int a = tid; a < n; a += SCAN_THREADS) {
+    const int t = a / k, e = idx[a];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E))
+      atomicOr(&mask[e * WORDS + (t >> 6)], 1ull << (t & 63));
+  }
+  __syncthreads();
+  int c = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int w = 0; w < WORDS; ++w) c += __popcll(mask[tid * WORDS + w]);
+    counts[tid] = c;
+  }
+  const int incl = block_inclusive_scan(sc, tid < E ? c : 0);
+  if (tid < E) {
+    off_s[tid] = incl - c;
+    offsets[tid] = incl - c;
+    if (tid == E - 1) {
+      off_s[E] = incl;
+      offsets[E] = incl;
+    }
+  }
+  __syncthreads();
+  for (int a = tid; a < n; a += SCAN_THREADS) {
+    const int t = a / k, e = idx[a];
+    if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) {
+      row_of_slot[a] = -1;
+      continue;
+    }
+    int r = off_s[e];
+    const int w = t >> 6;
+    for (int ww = 0; ww < w; ++ww) r += __popcll(mask[e * WORDS + ww]);
+    r += __popcll(mask[e * WORDS + w] & ((1ull << (t & 63)) - 1ull));
+    row_token[r] = t;
+    row_of_slot[a] = r;
+  }
+  if (!tiles) return;
+  // M-tiles of each group, groups in id order
+  const int nt = tid < E ? (c + bm - 1) / bm : 0;
+  const int tincl = block_inclusive_scan(sc, nt);
+  if (tid < E) {
+    const int base = tincl - nt;
+    for (int i = 0; i < nt && base + i < max_tiles; ++i) {
+      GTile tl;
+      tl.group = tid;
+      tl.row0 = off_s[tid] + i * bm;
+      tl.row1 = min(off_s[tid] + (i + 1) * bm, off_s[tid + 1]);
+      tl.pad = 0;
+      tiles[base + i] = tl;
+    }
+  }
+  if (tid == SCAN_THREADS - 1) n_tiles[0] = min(tincl, max_tiles);
+}
+
 }  // namespace
 
 int perm_blocks(int T) { return (T + PB - 1) / PB; }
+
+int perm_small_max_tokens() { return PB; }
+
+hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int32_t* counts,
+                                int32_t* offsets, int32_t* row_token, int32_t* row_of_slot, int bm,
+                                int max_tiles, GTile* tiles, int32_t* n_tiles, hipStream_t s) {
+  perm_small_kernel<<<1, SCAN_THREADS, 0, s>>>(idx, T, k, E, counts, offsets, row_token, row_of_slot,
+                                               bm, max_tiles, tiles, n_tiles);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* blk, int32_t* local_rank,
                           int32_t* counts, int32_t* offsets, int32_t* row_token,

@@ -12,42 +12,43 @@
 namespace moe {
 namespace {
 
-constexpr int WAVES_PER_BLOCK = 4;
-
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-// The router product may arrive as `splits` partial sums (a K-split GEMM);
-// they are added here in slice order, so the logits are deterministic.
-template <int EPL>
-__global__ __launch_bounds__(64 * WAVES_PER_BLOCK) void topk_softmax_kernel(
+// One block per token.  The router product may arrive as `splits` partial sums
+// (a K-split GEMM): all threads of the block add them in slice order into LDS
+// (so the logits are deterministic), then wavefront 0 selects the top k.
+// Blocks are 256 threads when there are partial sums to add, else one wavefront.
+template <int EPL, int TOPK_THREADS>
+__global__ __launch_bounds__(TOPK_THREADS) void topk_softmax_kernel(
     const float* __restrict__ part, int splits, float* __restrict__ logits_out, int T, int E,
     int k, int32_t* __restrict__ idx, float* __restrict__ wout) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * WAVES_PER_BLOCK + (threadIdx.x >> 6);
-  if (t >= T) return;
+  __shared__ float lg[64 * EPL];
+  const int t = blockIdx.x;
   const int64_t slice = static_cast<int64_t>(T) * E;
   const float* row = part + static_cast<int64_t>(t) * E;
+  for (int e = threadIdx.x; e < E; e += TOPK_THREADS) {
+    float l = row[e];
+    for (int s0 = 1; s0 < splits; s0 += 8) {
+      float pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = s0 + u < splits ? row[(s0 + u) * slice + e] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < splits) l += pv[u];
+    }
+    lg[e] = l;
+    if (logits_out) logits_out[static_cast<int64_t>(t) * E + e] = l;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
   float v[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + 64 * j;
-    float l = -__builtin_inff();
-    if (e < E) {
-      // load up to 8 slices at a time, then add them in slice order
-      l = row[e];
-      for (int s0 = 1; s0 < splits; s0 += 8) {
-        float pv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) pv[u] = s0 + u < splits ? row[(s0 + u) * slice + e] : 0.f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (s0 + u < splits) l += pv[u];
-      }
-      if (logits_out) logits_out[static_cast<int64_t>(t) * E + e] = l;
-    }
-    v[j] = l;
+    v[j] = e < E ? lg[e] : -__builtin_inff();
   }
   uint32_t taken = 0;
   float my_v = 0.f, top_v = 0.f;
@@ -90,23 +91,31 @@ __global__ __launch_bounds__(64 * WAVES_PER_BLOCK) void topk_softmax_kernel(
   }
 }
 
+template <int EPL, int THREADS>
+void go(const float* part, int splits, float* logits_out, int T, int E, int k, int32_t* idx,
+        float* w, hipStream_t s) {
+  topk_softmax_kernel<EPL, THREADS><<<T, THREADS, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
+}
+
 }  // namespace
 
 hipError_t launch_topk_softmax(const float* part, int splits, float* logits_out, int T, int E,
                                int k, int32_t* idx, float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((T + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK), block(64 * WAVES_PER_BLOCK);
   const int epl = (E + 63) / 64;
-  if (epl <= 1)
-    topk_softmax_kernel<1><<<grid, block, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
-  else if (epl <= 2)
-    topk_softmax_kernel<2><<<grid, block, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
-  else if (epl <= 4)
-    topk_softmax_kernel<4><<<grid, block, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
-  else if (epl <= 8)
-    topk_softmax_kernel<8><<<grid, block, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
-  else
-    topk_softmax_kernel<16><<<grid, block, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
+  if (splits > 1) {
+    if (epl <= 1) go<1, 256>(part, splits, logits_out, T, E, k, idx, w, s);
+    else if (epl <= 2) go<2, 256>(part, splits, logits_out, T, E, k, idx, w, s);
+    else if (epl <= 4) go<4, 256>(part, splits, logits_out, T, E, k, idx, w, s);
+    else if (epl <= 8) go<8, 256>(part, splits, logits_out, T, E, k, idx, w, s);
+    else go<16, 256>(part, splits, logits_out, T, E, k, idx, w, s);
+  } else {
+    if (epl <= 1) go<1, 64>(part, splits, logits_out, T, E, k, idx, w, s);
+    else if (epl <= 2) go<2, 64>(part, splits, logits_out, T, E, k, idx, w, s);
+    else if (epl <= 4) go<4, 64>(part, splits, logits_out, T, E, k, idx, w, s);
+    else if (epl <= 8) go<8, 64>(part, splits, logits_out, T, E, k, idx, w, s);
+    else go<16, 64>(part, splits, logits_out, T, E, k, idx, w, s);
+  }
   return hipGetLastError();
 }
 
