@@ -63,11 +63,21 @@ constexpr bool kTiledReady = true;
 #endif
 
 
+// The tiled GEMM's 32-bit offsets cover every operand of the expert FFNs.
+bool tiled_fits(const moe_problem_t* p) {
+  const int64_t T = p->T, Tk = T * p->k, D = p->D, I = p->I, Is = p->I_shared;
+  const int km = tiled_k_multiple();
+  if (D % km || I % km || Is % km) return false;
+  return tiled_offsets_fit(T, D, 2 * I, D, p->w_dtype) && tiled_offsets_fit(Tk, I, D, I, p->w_dtype) &&
+         (!Is || (tiled_offsets_fit(T, D, 2 * Is, D, p->shared_w_dtype) &&
+                  tiled_offsets_fit(T, Is, D, Is, p->shared_w_dtype)));
+}
+
 Plan make_plan(const moe_problem_t* p, double mean_rows) {
-  const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16;
+  const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16 && tiled_fits(p);
   int policy = p->tile_policy;
   if (policy == MOE_TILE_AUTO) policy = (tiled_ok && mean_rows > 48.0) ? MOE_TILE_LDS : MOE_TILE_STREAM;
-  if (policy == MOE_TILE_LDS && tiled_ok) return Plan{true, 0, 128};
+  if (policy == MOE_TILE_LDS && tiled_ok) return Plan{true, 0, tiled_bm()};
   int mt = mean_rows <= 4.0 ? 1 : mean_rows <= MOE_MT2_MEAN ? 2 : 4;
   mt = std::min(mt, stream_max_mt(p->act_dtype));
   return Plan{false, mt, 16 * mt};
@@ -77,16 +87,29 @@ int routed_tile_ub(int64_t rows, int groups, int bm) {
   return static_cast<int>(std::min<int64_t>(groups, rows) + rows / bm);
 }
 
-int blocks_per_m(const Plan& pl, bool gated, int n_out) {
-  if (pl.tiled) return tiled_blocks_n(gated, n_out);
+int blocks_per_m(const Plan& pl, bool wide, bool gated, int n_out) {
+  if (pl.tiled) return tiled_blocks_n(wide, gated, n_out);
   return (stream_waves_n(gated, n_out) + 3) / 4;
+}
+
+// Tiled launches use the wide block (512 weight rows) unless the narrow one
+// (256) pads the output columns of the launch's sets less.
+bool pick_wide(const GArgs& g, bool gated) {
+  int64_t pad_w = 0, pad_n = 0;
+  for (int i = 0; i < g.nsets; ++i) {
+    const int n = g.s[i].n_out, ww = gated ? 256 : 512, wn = gated ? 128 : 256;
+    pad_w += static_cast<int64_t>(tiled_blocks_n(true, gated, n)) * ww - n;
+    pad_n += static_cast<int64_t>(tiled_blocks_n(false, gated, n)) * wn - n;
+  }
+  return pad_w <= pad_n;
 }
 
 void finish_grid(GArgs& g, const Plan& pl, bool gated) {
   int b = 0;
+  g.wide = pl.tiled && pick_wide(g, gated);
   for (int i = 0; i < g.nsets; ++i) {
     GSet& S = g.s[i];
-    S.blocks_per_m = blocks_per_m(pl, gated, S.n_out);
+    S.blocks_per_m = blocks_per_m(pl, g.wide, gated, S.n_out);
     S.block0 = b;
     S.bm = pl.bm;
     b += S.m_slots * S.blocks_per_m * std::max(1, S.ksplit);
@@ -99,8 +122,9 @@ void finish_grid(GArgs& g, const Plan& pl, bool gated) {
 // partial sums the top-k kernel adds in slice order, so enough wavefronts
 // stream the router weight.
 Plan router_plan(const moe_problem_t* p) {
-  if (kTiledReady && p->act_dtype == MOE_BF16 && p->T >= 1024 && p->tile_policy != MOE_TILE_STREAM)
-    return Plan{true, 0, 128};
+  if (kTiledReady && p->act_dtype == MOE_BF16 && p->T >= 1024 && p->tile_policy != MOE_TILE_STREAM &&
+      p->D % tiled_k_multiple() == 0 && tiled_offsets_fit(p->T, p->D, p->E, p->D, p->act_dtype))
+    return Plan{true, 0, tiled_bm()};
   int mt = p->T <= 16 ? 1 : p->T <= 32 ? 2 : 4;
   mt = std::min(mt, stream_max_mt(p->act_dtype));
   return Plan{false, mt, 16 * mt};
@@ -110,7 +134,7 @@ Plan router_plan(const moe_problem_t* p) {
 // wavefronts) to cover the GPU, each slice a multiple of 64 and >= 256 long.
 int router_splits(const moe_problem_t* p, const Plan& pl) {
   const int64_t m_tiles = (p->T + pl.bm - 1) / pl.bm;
-  const int64_t items = pl.tiled ? m_tiles * tiled_blocks_n(false, p->E)
+  const int64_t items = pl.tiled ? m_tiles * tiled_blocks_n(p->E >= 512, false, p->E)
                                  : m_tiles * stream_waves_n(false, p->E);
   int s = 1;
   const int K = p->D;
@@ -120,7 +144,7 @@ int router_splits(const moe_problem_t* p, const Plan& pl) {
 
 hipError_t run_gemm(const GArgs& g, const Plan& pl, bool gated, int a_dt, int w_dt, int o_dt,
                     hipStream_t s) {
-  if (pl.tiled) return launch_tiled_gemm(g, pl.bm, gated, w_dt, o_dt, s);
+  if (pl.tiled) return launch_tiled_gemm(g, g.wide != 0, gated, w_dt, o_dt, s);
   return launch_stream_gemm(g, pl.mt, gated, a_dt, w_dt, o_dt, s);
 }
 

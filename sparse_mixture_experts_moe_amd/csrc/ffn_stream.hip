@@ -16,9 +16,12 @@
 // A-operand load instead of a materialised permuted copy).
 //
 // The K loop is software-pipelined over two register stages of 32*U elements.
-// Lane group q = lane/16 holds a contiguous run of 8*U K-elements of its row,
-// used 8 at a time by successive MFMAs; A and B use the same K assignment, so
-// each MFMA still contracts matching elements.
+// In MFMA step u of a stage, lane group q = lane/16 supplies K elements
+// [32u + 8q, 32u + 8q + 8) (bf16 / fp32 weights) or, for fp8 weights whose
+// 16-byte loads cover two steps, [64(u/2) + 16q + 8(u%2), +8).  Either way the
+// four lane groups of one 16-byte load instruction read 64 contiguous bytes of
+// each weight row, and A and B use the same K assignment, so each MFMA still
+// contracts matching elements.
 //
 // fp8 e4m3fn weights are decoded exactly to bf16 (v_cvt_scalef32_pk_bf16_fp8,
 // scale 1) and their per-output-channel fp32 scale is applied after the
@@ -99,7 +102,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
         arow = 0;
       }
     }
-    ap[mc] = a_base + (arow * S.lda + k_beg + q * 8 * U) * Elt<ADT>::bytes;
+    ap[mc] = a_base + (arow * S.lda + k_beg) * Elt<ADT>::bytes;
   }
   const char* w_base = static_cast<const char*>(S.w) + group * S.w_gstride * Elt<WDT>::bytes;
   const char* bp[NF];
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
       bv[f] = n < n_out;
       if (!bv[f]) n = 0;
     }
-    bp[f] = w_base + (static_cast<int64_t>(n) * K + k_beg + q * 8 * U) * Elt<WDT>::bytes;
+    bp[f] = w_base + (static_cast<int64_t>(n) * K + k_beg) * Elt<WDT>::bytes;
   }
 
   f32x4 acc[MT][NF];
@@ -126,19 +129,31 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
 
   uint4 sa0[MT][AV], sb0[NF][BV], sa1[MT][AV], sb1[NF][BV];
 
+  // byte offset of 16-byte vector v of a stage, for operand dtype DT, in the K
+  // assignment described at the top of the file
+  auto voff = [&](int dt_bytes, int v) __attribute__((always_inline)) -> int {
+    if (dt_bytes == 1) return v * 64 + q * 16;                         // fp8 weights: pairs of steps
+    if (dt_bytes == 4) return (v >> 1) * 128 + q * 32 + (v & 1) * 16;  // fp32: two vectors per step
+    if (WDT == DT_FP8) return (v >> 1) * 128 + q * 32 + (v & 1) * 16;  // bf16 A beside fp8 weights
+    return v * 64 + q * 16;                                            // bf16, one vector per step
+  };
   auto load = [&](uint4 (&sa)[MT][AV], uint4 (&sb)[NF][BV], int stage) __attribute__((always_inline)) {
     const int64_t koff = static_cast<int64_t>(stage) * KS;
 #pragma unroll
     for (int f = 0; f < NF; ++f) {
-      const uint4* p = reinterpret_cast<const uint4*>(bp[f] + koff * Elt<WDT>::bytes);
+      const char* p = bp[f] + koff * Elt<WDT>::bytes;
 #pragma unroll
-      for (int v = 0; v < BV; ++v) sb[f][v] = bv[f] ? load_w(p + v) : uint4{0, 0, 0, 0};
+      for (int v = 0; v < BV; ++v)
+        sb[f][v] = bv[f] ? load_w(reinterpret_cast<const uint4*>(p + voff(Elt<WDT>::bytes, v)))
+                         : uint4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int mc = 0; mc < MT; ++mc) {
-      const uint4* p = reinterpret_cast<const uint4*>(ap[mc] + koff * Elt<ADT>::bytes);
+      const char* p = ap[mc] + koff * Elt<ADT>::bytes;
 #pragma unroll
-      for (int v = 0; v < AV; ++v) sa[mc][v] = av[mc] ? p[v] : uint4{0, 0, 0, 0};
+      for (int v = 0; v < AV; ++v)
+        sa[mc][v] = av[mc] ? *reinterpret_cast<const uint4*>(p + voff(Elt<ADT>::bytes, v))
+                           : uint4{0, 0, 0, 0};
     }
   };
 

@@ -6,149 +6,180 @@
 // "Ling-2.6-1T with SGLang-JAX", section 4: keep tokens and accumulators
 // resident and stream the expert weights with the next tile's fetch in flight).
 //
-// Block tile: 128 sorted rows of one group x 256 weight rows; K is staged 32
-// elements at a time through two LDS buffers (48 KiB), and the global loads of
-// stage s+1 are in flight while the MFMAs of stage s run.  The block is small
-// enough in registers (128 accumulators per lane) and LDS for two blocks to be
-// resident on a CU, so one block's MFMAs cover the other's barrier and LDS
-// waits.  4 wavefronts in a 2 x 2 grid each own 64 rows x 128 weight rows and
-// issue 16x16x32 bf16 MFMAs with the weight fragment as the M operand, so a
-// lane's accumulator holds 4 consecutive output columns of one row.  For the
-// fused gate/up projection the 256 weight rows are 128 gate rows and the 128
-// matching up rows; a wavefront holds the gate and up halves of the same 64 h
-// columns and forms act(gate)*up in registers (the packed gate/up tile of GMM
-// v2 on the Ironwood page).
+// Block tile: 128 sorted rows of one group x BNW weight rows.  Two shapes are
+// built: "wide" (BNW = 512, 8 wavefronts, one block per CU) for the expert
+// FFNs and "narrow" (BNW = 256, 4 wavefronts, two blocks per CU) for narrow
+// outputs.  Either way every SIMD runs two wavefronts of 64 rows x 128 weight
+// rows (128 accumulators each, in AGPRs), which is what it takes to keep the
+// matrix cores busy; 16x16x32 bf16 MFMAs take the weight fragment as the M
+// operand, so a lane's accumulator holds 4 consecutive output columns of one
+// row.  For the fused gate/up projection the BNW weight rows are BNW/2 gate
+// rows and the matching BNW/2 up rows; each wavefront holds the gate and up
+// halves of the same 64 h columns and forms act(gate)*up in registers (the
+// packed gate/up tile of GMM v2 on the Ironwood page).
+//
+// K is staged 32 elements at a time through a ring of S LDS buffers filled by
+// direct HBM -> LDS loads (global_load_lds_dwordx4: a lane's 16 bytes land at
+// the instruction's LDS base + 16 x lane).  Stage st+S is fetched while stage
+// st is multiplied, and a wavefront's fragments for stage st+1 are read from
+// LDS while its MFMAs of stage st run, so neither the fetch latency nor the
+// LDS latency sits in front of the matrix cores; the copies of a stage are
+// spread between the MFMA groups.  One barrier per stage publishes a stage's
+// copies and frees the slot that was read before.
 //
 // LDS rows hold 32 bf16 (64 bytes, 4 chunks of 16); chunk c of row r sits at
-// c ^ ((r >> 1) & 3), which keeps the 16-byte copy stores and fragment reads
-// free of bank conflicts.  fp8 e4m3fn weights stay fp8 in LDS (32-byte rows of
-// four 8-byte chunks, chunk c of row r at c ^ ((r >> 2) & 3)) and are decoded
-// exactly to bf16 as fragments are read, which halves the weight tile's LDS
-// traffic; per-channel scales are applied after the reduction.
-//
-// Blocks are remapped so that consecutive tiles (the M-tiles and N-blocks of
-// one expert) run on the same XCD and share its L2; the remap spans only the
-// tiles that exist, so empty tile slots of the grid cost nothing.
+// c ^ ((r >> 1) & 3), which keeps the fragment reads free of bank conflicts.
+// Since a copy lane's LDS position is fixed by its lane index, the swizzle is
+// applied on the source side: the lane that fills a position fetches the
+// chunk that belongs there.  fp8 e4m3fn weights stay fp8 in LDS (32-byte rows
+// of two 16-byte halves, half h of row r at h ^ ((r >> 3) & 1)) and are decoded
+// exactly to bf16 when a stage's fragments are taken up, which halves the
+// weight tile's LDS footprint; per-channel scales are applied after the
+// reduction.
+#include <type_traits>
+
 #include "moe_kernels.h"
 
 namespace moe {
 namespace {
 
-// Build-time tuning knob: MOE_TILED_REMAP 1 = XCD-aware block order.
-#ifndef MOE_TILED_REMAP
-#define MOE_TILED_REMAP 0
-#endif
-
-constexpr int BNW = 256;                  // weight rows per block
+constexpr int BM = 128;                   // rows per M-tile
 constexpr int BK = 32;                    // K elements per stage
-constexpr int NSTAGE = 2;                 // LDS buffers
-constexpr int THREADS = 256;
 constexpr int ROWB = BK * 2;              // LDS bytes per bf16 tile row (64)
 constexpr int ROWB8 = BK;                 // LDS bytes per fp8 tile row (32)
-constexpr int NXCD = 8;
+constexpr int LDS_CU = 160 * 1024;        // LDS per CU
 
-template <int BM, bool FP8> struct Cfg {
+template <int BNW_, int WN_, int BPC_, bool FP8> struct Cfg {
+  static constexpr int BNW = BNW_;                    // weight rows per block
+  static constexpr int WM = 2, WN = WN_;              // wavefront grid (rows x weights)
+  static constexpr int NW = WM * WN;
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BPC = BPC_;                    // blocks per CU
+  static constexpr int TF = BM / WM / 16;             // row fragments per wavefront (4)
+  static constexpr int WF = BNW / WN / 16;            // weight fragments per wavefront (8)
   static constexpr int A_BYTES = BM * ROWB;
   static constexpr int B_BYTES = BNW * (FP8 ? ROWB8 : ROWB);
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int WM = BM / 2;           // rows per wavefront
-  static constexpr int TF = WM / 16;          // row (token) fragments per wavefront
-  static constexpr int AL = BM / 64;          // A chunks per thread per stage
-  static constexpr int LDS = NSTAGE * STAGE;
+  static constexpr int S0 = LDS_CU / BPC / STAGE;
+  static constexpr int S = S0 > 6 ? 6 : S0;           // LDS ring depth
+  static constexpr int LDS = S * STAGE;
+  static constexpr int AL = A_BYTES / 1024 / NW;      // 1 KiB copy instructions per wavefront, A
+  static constexpr int BL = B_BYTES / 1024 / NW;      // same, B
+  static constexpr int P = AL + BL;
+  static_assert(AL * NW * 1024 == A_BYTES && BL * NW * 1024 == B_BYTES, "copy split");
+  static_assert(S >= 3, "ring depth");
 };
 
+// byte offset of 16-byte chunk c of bf16 tile row r
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * ROWB + ((chunk ^ ((row >> 1) & 3)) << 4);
 }
-__device__ __forceinline__ int swz8(int row, int chunk) {
-  return row * ROWB8 + ((chunk ^ ((row >> 2) & 3)) << 3);
+// 16-byte half of fp8 tile row r that holds logical half h (an involution)
+__device__ __forceinline__ int half8(int row, int h) { return h ^ ((row >> 3) & 1); }
+
+// HBM -> LDS copy of 16 bytes per lane from sbase + voff to lds + 16 * lane;
+// sbase and lds are wave-uniform.  Issued through inline asm so the compiler
+// does not conservatively wait for every copy in flight before each LDS read;
+// completion is tracked explicitly with wait_vm below.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, const void* lds) {
+  const uint32_t l = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds))));
+  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const uint64_t bs = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bs), "s"(l)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// A wave-uniform pointer, held in scalar registers.
+template <class T> __device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32)));
+  return reinterpret_cast<T*>(static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32));
 }
 
-#if MOE_TILED_REMAP
-// Logical tile of a physical block: consecutive logical tiles share an XCD.
-__device__ __forceinline__ bool remap_block(const GArgs& g, int& logical) {
-  int real = 0;
-  for (int i = 0; i < g.nsets; ++i) {
-    const GSet& S = g.s[i];
-    const int m = S.tiles ? min(S.n_tiles[0], S.m_slots) : S.m_slots;
-    real += m * S.blocks_per_m * (S.ksplit > 1 ? S.ksplit : 1);
-  }
-  const int per_xcd = (real + NXCD - 1) / NXCD;
-  const int b = blockIdx.x;
-  const int slot = b / NXCD;
-  if (slot >= per_xcd) return false;
-  logical = (b % NXCD) * per_xcd + slot;
-  if (logical >= real) return false;
-  // turn the dense logical index back into the grid numbering resolve_block uses
-  int acc = 0;
-  for (int i = 0; i < g.nsets; ++i) {
-    const GSet& S = g.s[i];
-    const int m = S.tiles ? min(S.n_tiles[0], S.m_slots) : S.m_slots;
-    const int n = m * S.blocks_per_m * (S.ksplit > 1 ? S.ksplit : 1);
-    if (logical < acc + n) {
-      logical = S.block0 + (logical - acc);
-      return true;
-    }
-    acc += n;
-  }
-  return false;
+// Wait until at most N of this wavefront's vector-memory operations are in
+// flight (they complete in order).
+template <int N> __device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-#endif
+// Wait for all but the newest `newer` groups of P copies (newer <= M).
+template <int P, int M> __device__ __forceinline__ void wait_newer(int newer) {
+  if constexpr (M == 0) {
+    wait_vm<0>();
+  } else {
+    if (newer >= M) wait_vm<M * P>();
+    else wait_newer<P, M - 1>(newer);
+  }
+}
 
-template <int BM, bool GATED, int WDT, int ODT>
-__global__ __launch_bounds__(THREADS, 2) void tiled_gemm_kernel(const GArgs g) {
-  using C = Cfg<BM, WDT == DT_FP8>;
+template <class C, bool GATED, int WDT, int ODT>
+__global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g) {
+  constexpr bool FP8 = WDT == DT_FP8;
+  constexpr int TF = C::TF, WF = C::WF, S = C::S, P = C::P, BNW = C::BNW;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   // An (empty) statement that names an accumulation register makes the backend
   // select the AGPR form of the MFMAs, so the accumulators live in AGPRs and
-  // the VGPRs stay free for fragments and the copy pipeline.
+  // the VGPRs stay free for fragments.
   asm volatile("" ::: "a0");
-  int b = blockIdx.x;
-#if MOE_TILED_REMAP
-  if (!remap_block(g, b)) return;
-#endif
+  const int b = blockIdx.x;
   int si, group, row0, row1, nblk;
   if (!resolve_block(g, b, si, group, row0, row1, nblk)) return;
-  const GSet& S = g.s[si];
+  // the tile is the same for the whole block: keep it (and everything derived
+  // from it, such as the copy base addresses) in scalar registers
+  si = __builtin_amdgcn_readfirstlane(si);
+  group = __builtin_amdgcn_readfirstlane(group);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  row1 = __builtin_amdgcn_readfirstlane(row1);
+  nblk = __builtin_amdgcn_readfirstlane(nblk);
+  const GSet& Sg = g.s[si];
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % C::WM, wn = wave / C::WM;
   const int lr = lane & 15, q = lane >> 4;
-  const int K = S.K;
-  const int split = S.ksplit > 1 ? (b - S.block0) % S.ksplit : 0;
-  const int k_len = S.ksplit > 1 ? K / S.ksplit : K;
+  const int K = Sg.K;
+  const int split = Sg.ksplit > 1 ? (b - Sg.block0) % Sg.ksplit : 0;
+  const int k_len = Sg.ksplit > 1 ? K / Sg.ksplit : K;
   const int k_beg = split * k_len;
   const int nst = k_len / BK;
-  const int n_out = S.n_out;
+  const int n_out = Sg.n_out;
   const int n0 = nblk * (GATED ? BNW / 2 : BNW);   // first h column (gated) / output column
 
-  // ---- global -> LDS copy assignments (A: BM rows x 4 chunks, thread: chunk tid%4).
-  // Rows past the tile and weight rows past n_out are loaded from a valid row
-  // instead: they only feed accumulator rows / columns the epilogue never stores,
-  // so the copy needs no per-load predication.
-  const int cc = tid & 3;
-  const char* a_ptr[C::AL];
+  // ---- HBM -> LDS copy assignments.  Copy instruction j of a stage fills LDS
+  // bytes [1024 j, 1024 j + 1024) of the A or B tile; lane l fills the 16 bytes
+  // at 1024 j + 16 l.  Offsets are 32-bit from a wave-uniform base (checked by
+  // the launcher).  Rows past the tile and weight rows past n_out are fetched
+  // from a valid row instead: they only feed accumulator rows / columns the
+  // epilogue never stores, so the copy needs no predication.
+  const char* a_base = uniform_ptr(static_cast<const char*>(Sg.a) + static_cast<int64_t>(k_beg) * 2);
+  uint32_t a_off[C::AL];
 #pragma unroll
   for (int i = 0; i < C::AL; ++i) {
-    const int r = row0 + (tid >> 2) + 64 * i;
+    const int j = wave * C::AL + i;
+    const int tr = 16 * j + (lane >> 2);             // 4 lanes per 64-byte row
+    const int c = (lane & 3) ^ ((tr >> 1) & 3);      // logical chunk of this position
+    const int r = row0 + tr;
     int64_t arow = 0;
     if (r < row1) {
-      arow = S.gather ? S.gather[r] : r;
-      if (static_cast<uint64_t>(arow) >= static_cast<uint64_t>(S.a_rows)) arow = 0;  // caller error
+      arow = Sg.gather ? Sg.gather[r] : r;
+      if (static_cast<uint64_t>(arow) >= static_cast<uint64_t>(Sg.a_rows)) arow = 0;  // caller error
     }
-    a_ptr[i] = static_cast<const char*>(S.a) + (arow * S.lda + k_beg + cc * 8) * 2;
+    a_off[i] = static_cast<uint32_t>((arow * Sg.lda + c * 8) * 2);
   }
-  // B: bf16 -> 4 rows x 16 B per thread; fp8 -> 2 rows x 16 B (32 codes, 2 LDS chunks each)
-  constexpr bool FP8 = WDT == DT_FP8;
-  constexpr int BL = FP8 ? 2 : 4;
-  constexpr int BSTEP = FP8 ? 128 : 64;
-  const int bcol = FP8 ? (tid & 1) : cc;
-  const int brow0 = FP8 ? (tid >> 1) : (tid >> 2);
-  const char* wg = static_cast<const char*>(S.w) + group * S.w_gstride * (FP8 ? 1 : 2);
-  const char* b_ptr[BL];
+  const char* b_base = uniform_ptr(static_cast<const char*>(Sg.w) +
+                                   (group * Sg.w_gstride + k_beg) * (FP8 ? 1 : 2));
+  uint32_t b_off[C::BL];
 #pragma unroll
-  for (int i = 0; i < BL; ++i) {
-    const int tr = brow0 + BSTEP * i;
+  for (int i = 0; i < C::BL; ++i) {
+    const int j = wave * C::BL + i;
+    // bf16: 4 lanes per 64-byte row; fp8: 2 lanes per 32-byte row
+    const int tr = FP8 ? 32 * j + (lane >> 1) : 16 * j + (lane >> 2);
     int wrow;
     if (GATED) {
       const int n = n0 + (tr & (BNW / 2 - 1));
@@ -156,114 +187,146 @@ __global__ __launch_bounds__(THREADS, 2) void tiled_gemm_kernel(const GArgs g) {
     } else {
       wrow = n0 + tr < n_out ? n0 + tr : 0;
     }
-    b_ptr[i] = FP8 ? wg + static_cast<int64_t>(wrow) * K + k_beg + bcol * 16
-                   : wg + (static_cast<int64_t>(wrow) * K + k_beg + bcol * 8) * 2;
+    b_off[i] = FP8 ? static_cast<uint32_t>(static_cast<int64_t>(wrow) * K + half8(tr, lane & 1) * 16)
+                   : static_cast<uint32_t>((static_cast<int64_t>(wrow) * K +
+                                            ((lane & 3) ^ ((tr >> 1) & 3)) * 8) * 2);
   }
-
-  // one register stage in flight
-  u32x4 ra[C::AL], rb[BL];
-  auto gload = [&](int st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < C::AL; ++i)
-      ra[i] = *reinterpret_cast<const u32x4*>(a_ptr[i] + st * (BK * 2));
-    const int64_t boff = static_cast<int64_t>(st) * BK * (FP8 ? 1 : 2);
-#pragma unroll
-    for (int i = 0; i < BL; ++i)
-      rb[i] = *reinterpret_cast<const u32x4*>(b_ptr[i] + boff);
-  };
-  auto lstore = [&](int buf) __attribute__((always_inline)) {
-    char* base = smem + buf * C::STAGE;
-#pragma unroll
-    for (int i = 0; i < C::AL; ++i)
-      *reinterpret_cast<u32x4*>(base + swz((tid >> 2) + 64 * i, cc)) = ra[i];
-    char* bb = base + C::A_BYTES;
-#pragma unroll
-    for (int i = 0; i < BL; ++i) {
-      const int tr = brow0 + BSTEP * i;
-      if constexpr (FP8) {
-        const u32x4 v = rb[i];
-        *reinterpret_cast<uint2*>(bb + swz8(tr, 2 * bcol)) = uint2{v[0], v[1]};
-        *reinterpret_cast<uint2*>(bb + swz8(tr, 2 * bcol + 1)) = uint2{v[2], v[3]};
-      } else {
-        *reinterpret_cast<u32x4*>(bb + swz(tr, cc)) = rb[i];
-      }
+  // copy instruction k (0..P-1) of stage st: the A instructions, then B
+  auto issue_one = [&](int st, int k) __attribute__((always_inline)) {
+    char* base = smem + (st % S) * C::STAGE;
+    if (k < C::AL) {
+      dma16(a_off[k], a_base + st * (BK * 2), base + (wave * C::AL + k) * 1024);
+    } else {
+      const int i = k - C::AL;
+      dma16(b_off[i], b_base + st * (FP8 ? BK : BK * 2),
+            base + C::A_BYTES + (wave * C::BL + i) * 1024);
     }
   };
 
   // acc[f][i]: weight fragment f (16 weight rows) x row fragment i (16 rows)
-  f32x4 acc[8][C::TF];
+  f32x4 acc[WF][TF];
 #pragma unroll
-  for (int f = 0; f < 8; ++f)
+  for (int f = 0; f < WF; ++f)
 #pragma unroll
-    for (int i = 0; i < C::TF; ++i) acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < TF; ++i) acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf) __attribute__((always_inline)) {
-    const char* base = smem + buf * C::STAGE;
+  // weight tile row of fragment f of this wavefront
+  auto wrow_of = [&](int f) __attribute__((always_inline)) -> int {
+    constexpr int HC = BNW / 2 / C::WN;   // h columns per wavefront (gated)
+    return GATED ? ((f < WF / 2 ? 0 : BNW / 2) + wn * HC + (f % (WF / 2)) * 16 + lr)
+                 : (wn * WF * 16 + f * 16 + lr);
+  };
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  using BT = typename std::conditional<FP8, u32x2, bf16x8>::type;
+  struct Frag {
+    bf16x8 a[TF];
+    BT b[WF];
+    bf16x8 w[FP8 ? WF : 1];
+  };
+  auto readf = [&](Frag& F, int st) __attribute__((always_inline)) {
+    const char* base = smem + (st % S) * C::STAGE;
     const char* bb = base + C::A_BYTES;
-    bf16x8 wf[8], tf[C::TF];
 #pragma unroll
-    for (int f = 0; f < 8; ++f) {
-      const int tr = GATED ? ((f < 4 ? 0 : BNW / 2) + wn * 64 + (f & 3) * 16 + lr)
-                           : (wn * 128 + f * 16 + lr);
-      if constexpr (WDT == DT_FP8) {
-        const uint2 raw = *reinterpret_cast<const uint2*>(bb + swz8(tr, q));
-        wf[f] = fp8x8_to_bf16x8(raw.x, raw.y);
-      } else {
-        wf[f] = *reinterpret_cast<const bf16x8*>(bb + swz(tr, q));
-      }
+    for (int i = 0; i < TF; ++i)
+      F.a[i] = *reinterpret_cast<const bf16x8*>(base + swz(wm * TF * 16 + 16 * i + lr, q));
+#pragma unroll
+    for (int f = 0; f < WF; ++f) {
+      const int tr = wrow_of(f);
+      if constexpr (FP8)
+        F.b[f] = *reinterpret_cast<const u32x2*>(bb + tr * ROWB8 + half8(tr, q >> 1) * 16 + (q & 1) * 8);
+      else
+        F.b[f] = *reinterpret_cast<const bf16x8*>(bb + swz(tr, q));
     }
+  };
+  // Use the fragments in an empty statement so that the compiler's own wait
+  // for them lands here (before the barrier) and not in front of the MFMAs.
+  auto settle = [&](Frag& F) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < C::TF; ++i)
-      tf[i] = *reinterpret_cast<const bf16x8*>(base + swz(wm * C::WM + i * 16 + lr, q));
+    for (int i = 0; i < TF; ++i) asm volatile("" ::"v"(F.a[i]));
 #pragma unroll
-    for (int f = 0; f < 8; ++f)
+    for (int f = 0; f < WF; ++f) asm volatile("" ::"v"(F.b[f]));
+    if constexpr (FP8) {
 #pragma unroll
-      for (int i = 0; i < C::TF; ++i)
-        acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[f], tf[i], acc[f][i], 0, 0, 0);
+      for (int f = 0; f < WF; ++f) F.w[f] = fp8x8_to_bf16x8(F.b[f][0], F.b[f][1]);
+    }
+  };
+  // MFMAs of one stage; when dst >= 0 the copies of stage dst are spread
+  // between the weight-fragment groups so their issue overlaps the MFMAs.
+  auto mma = [&](const Frag& F, int dst) __attribute__((always_inline)) {
+    constexpr int PER = (P + WF - 1) / WF;
+#pragma unroll
+    for (int f = 0; f < WF; ++f) {
+      bf16x8 w;
+      if constexpr (FP8) w = F.w[f];
+      else w = F.b[f];
+#pragma unroll
+      for (int i = 0; i < TF; ++i)
+        acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, F.a[i], acc[f][i], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < PER; ++u)
+        if (f * PER + u < P && dst >= 0) issue_one(dst, f * PER + u);
+    }
+  };
+  // One stage: stage st+1 has landed (own copies; everyone's after the
+  // barrier, which also frees slot st % S for stage st+S); st+1's fragments
+  // are read while st's MFMAs run.
+  auto step = [&](Frag& cur, Frag& nxt, int st) __attribute__((always_inline)) {
+    wait_newer<P, S - 2>(max(0, min(S - 2, nst - 2 - st)));
+    settle(cur);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    readf(nxt, st + 1);          // st + 1 == nst reads a stale slot that is never used
+    mma(cur, st + S < nst ? st + S : -1);
   };
 
-  // ---- pipeline: stage s+1 is fetched into registers while stage s is
-  // multiplied out of LDS, then stored to the other buffer; one barrier per stage.
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const bool more = st + 1 < nst;
-    if (more) gload(st + 1);
-    compute(st & 1);
-    if (more) lstore((st + 1) & 1);
-    __syncthreads();
+  // ---- prologue: S stages in flight, stage 0's fragments read
+#pragma unroll
+  for (int st = 0; st < S; ++st)
+    if (st < nst)
+#pragma unroll
+      for (int k = 0; k < P; ++k) issue_one(st, k);
+  Frag F0, F1;
+  wait_newer<P, S - 1>(min(S - 1, nst - 1));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  readf(F0, 0);
+  for (int st = 0; st < nst; st += 2) {   // nst is even (checked by the launcher)
+    step(F0, F1, st);
+    step(F1, F0, st + 1);
   }
+  wait_vm<0>();   // no copy may still be in flight when the block retires
 
   // ---- epilogue: lane holds C[row lr of fragment i][cols 4q..4q+3 of fragment f];
-  // the 4 columns are stored together (8 bytes in bf16, 16 in fp32).
-  const float* sc = S.scale ? S.scale + group * S.s_gstride : nullptr;
-  constexpr int OCOLS = GATED ? 64 : 128;      // output columns per wavefront
-  const int col_w = n0 + wn * OCOLS;           // first output column of this wavefront
-  char* outb = static_cast<char*>(S.out) + split * S.split_stride * (ODT == DT_F32 ? 4 : 2);
+  // the 4 columns are stored together (8 bytes in bf16, 16 in fp32).  Column
+  // groups outermost, so each group's scales are loaded once and the
+  // accumulators are consumed in order.
+  const float* sc = Sg.scale ? Sg.scale + group * Sg.s_gstride : nullptr;
+  constexpr int OCOLS = GATED ? BNW / 2 / C::WN : BNW / C::WN;   // output columns per wavefront
+  const int col_w = n0 + wn * OCOLS;
+  char* outb = static_cast<char*>(Sg.out) + split * Sg.split_stride * (ODT == DT_F32 ? 4 : 2);
 #pragma unroll
-  for (int i = 0; i < C::TF; ++i) {
-    const int r = row0 + wm * C::WM + i * 16 + lr;
-    if (r >= row1) continue;
+  for (int f = 0; f < (GATED ? WF / 2 : WF); ++f) {
+    const int col = col_w + f * 16 + 4 * q;   // first of the lane's 4 columns
+    const bool col_ok = col < n_out;          // n_out is a multiple of 4
+    float s0[4], s1[4];
 #pragma unroll
-    for (int f = 0; f < (GATED ? 4 : 8); ++f) {
-      const int col = col_w + f * 16 + 4 * q;  // first of the lane's 4 columns
-      if (col >= n_out) continue;              // n_out is a multiple of 4
+    for (int j = 0; j < 4; ++j) {
+      s0[j] = (sc && col_ok) ? sc[col + j] : 1.f;
+      s1[j] = (GATED && sc && col_ok) ? sc[n_out + col + j] : 1.f;
+    }
+#pragma unroll
+    for (int i = 0; i < TF; ++i) {
+      const int r = row0 + wm * TF * 16 + i * 16 + lr;
+      if (r >= row1 || !col_ok) continue;
       float v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        if constexpr (GATED) {
-          float gv = acc[f][i][j], uv = acc[f + 4][i][j];
-          if (sc) {
-            gv *= sc[col + j];
-            uv *= sc[n_out + col + j];
-          }
-          v[j] = act_fn(S.act, gv) * uv;
-        } else {
-          v[j] = acc[f][i][j] * (sc ? sc[col + j] : 1.f);
-        }
+        if constexpr (GATED)
+          v[j] = act_fn(Sg.act, acc[f][i][j] * s0[j]) * (acc[f + WF / 2][i][j] * s1[j]);
+        else
+          v[j] = acc[f][i][j] * s0[j];
       }
-      const int64_t o = static_cast<int64_t>(r) * S.ldo + col;
+      const int64_t o = static_cast<int64_t>(r) * Sg.ldo + col;
       if constexpr (ODT == DT_BF16) {
         const uint32_t p0 = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
         const uint32_t p1 = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
@@ -275,41 +338,56 @@ __global__ __launch_bounds__(THREADS, 2) void tiled_gemm_kernel(const GArgs g) {
   }
 }
 
-template <int BM, bool GATED, int WDT, int ODT>
+template <class C, bool GATED, int WDT, int ODT>
 hipError_t launch_one(const GArgs& g, hipStream_t s) {
-  const int grid = MOE_TILED_REMAP ? (g.total_blocks + NXCD - 1) / NXCD * NXCD : g.total_blocks;
-  tiled_gemm_kernel<BM, GATED, WDT, ODT><<<grid, THREADS, 0, s>>>(g);
+  tiled_gemm_kernel<C, GATED, WDT, ODT><<<g.total_blocks, C::THREADS, 0, s>>>(g);
   return hipGetLastError();
 }
 
-template <int BM>
+template <int BNW, int WN, int BPC>
 hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, hipStream_t s) {
+  using CB = Cfg<BNW, WN, BPC, false>;
+  using C8 = Cfg<BNW, WN, BPC, true>;
   if (gated) {
-    if (w_dtype == DT_BF16 && out_dtype == DT_BF16) return launch_one<BM, true, DT_BF16, DT_BF16>(g, s);
-    if (w_dtype == DT_FP8 && out_dtype == DT_BF16) return launch_one<BM, true, DT_FP8, DT_BF16>(g, s);
+    if (w_dtype == DT_BF16 && out_dtype == DT_BF16) return launch_one<CB, true, DT_BF16, DT_BF16>(g, s);
+    if (w_dtype == DT_FP8 && out_dtype == DT_BF16) return launch_one<C8, true, DT_FP8, DT_BF16>(g, s);
   } else {
-    if (w_dtype == DT_BF16 && out_dtype == DT_BF16) return launch_one<BM, false, DT_BF16, DT_BF16>(g, s);
-    if (w_dtype == DT_FP8 && out_dtype == DT_BF16) return launch_one<BM, false, DT_FP8, DT_BF16>(g, s);
-    if (w_dtype == DT_BF16 && out_dtype == DT_F32) return launch_one<BM, false, DT_BF16, DT_F32>(g, s);
+    if (w_dtype == DT_BF16 && out_dtype == DT_BF16) return launch_one<CB, false, DT_BF16, DT_BF16>(g, s);
+    if (w_dtype == DT_FP8 && out_dtype == DT_BF16) return launch_one<C8, false, DT_FP8, DT_BF16>(g, s);
+    if (w_dtype == DT_BF16 && out_dtype == DT_F32) return launch_one<CB, false, DT_BF16, DT_F32>(g, s);
   }
   return hipErrorInvalidValue;
 }
+
+int block_width(bool wide) { return wide ? 512 : 256; }
 
 }  // namespace
 
-int tiled_blocks_n(bool gated, int n_out) {
-  return gated ? (n_out + BNW / 2 - 1) / (BNW / 2) : (n_out + BNW - 1) / BNW;
+int tiled_bm() { return BM; }
+
+int tiled_k_multiple() { return 2 * BK; }
+
+int tiled_blocks_n(bool wide, bool gated, int n_out) {
+  const int w = gated ? block_width(wide) / 2 : block_width(wide);
+  return (n_out + w - 1) / w;
 }
 
-hipError_t launch_tiled_gemm(const GArgs& g, int bm, bool gated, int w_dtype, int out_dtype,
+bool tiled_offsets_fit(int64_t a_rows, int64_t lda, int64_t w_rows, int64_t K, int w_dtype) {
+  const int64_t wb = w_dtype == DT_FP8 ? 1 : 2;
+  return a_rows * lda * 2 < (int64_t(1) << 32) && w_rows * K * wb < (int64_t(1) << 32);
+}
+
+hipError_t launch_tiled_gemm(const GArgs& g, bool wide, bool gated, int w_dtype, int out_dtype,
                              hipStream_t s) {
   if (g.total_blocks <= 0) return hipSuccess;
   for (int i = 0; i < g.nsets; ++i) {
-    const int ks = g.s[i].ksplit > 1 ? g.s[i].ksplit : 1;
-    if ((g.s[i].K / ks) % BK || g.s[i].bm != bm || g.s[i].n_out % 4) return hipErrorInvalidValue;
+    const GSet& S = g.s[i];
+    const int ks = S.ksplit > 1 ? S.ksplit : 1;
+    if ((S.K / ks) % (2 * BK) || S.bm != BM || S.n_out % 4) return hipErrorInvalidValue;
+    if (!tiled_offsets_fit(S.a_rows, S.lda, S.NB, S.K, w_dtype)) return hipErrorInvalidValue;
   }
-  if (bm == 128) return dispatch<128>(g, gated, w_dtype, out_dtype, s);
-  return hipErrorInvalidValue;
+  return wide ? dispatch<512, 4, 1>(g, gated, w_dtype, out_dtype, s)
+              : dispatch<256, 2, 2>(g, gated, w_dtype, out_dtype, s);
 }
 
 }  // namespace moe

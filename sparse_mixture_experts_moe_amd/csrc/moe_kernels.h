@@ -65,6 +65,7 @@ struct GArgs {
   GSet s[2];
   int32_t nsets;
   int32_t total_blocks;
+  int32_t wide;             // tiled kernel: 512 weight rows per block (host-side choice)
 };
 
 // ------------------------------------------------------------------ device helpers
@@ -160,11 +161,16 @@ hipError_t launch_stream_gemm(const GArgs& g, int mt, bool gated, int a_dtype, i
 int stream_waves_n(bool gated, int n_out);   // wave tiles along N per m-tile
 int stream_max_mt(int a_dtype);              // largest mt the stream kernel runs for a dtype
 
-// Grouped GEMM, LDS-tiled (bf16 activations, bf16 or fp8 weights); bm = 128 or
-// 256 rows per M-tile (every set's bm must match).
-hipError_t launch_tiled_gemm(const GArgs& g, int bm, bool gated, int w_dtype, int out_dtype,
+// Grouped GEMM, LDS-tiled (bf16 activations, bf16 or fp8 weights), M-tiles of
+// tiled_bm() rows (every set's bm must match).  wide: 512 weight rows per block
+// (one block per CU); otherwise 256 (two blocks per CU).
+hipError_t launch_tiled_gemm(const GArgs& g, bool wide, bool gated, int w_dtype, int out_dtype,
                              hipStream_t s);
-int tiled_blocks_n(bool gated, int n_out);
+int tiled_bm();
+int tiled_k_multiple();                      // every K (slice) must be a multiple of this
+int tiled_blocks_n(bool wide, bool gated, int n_out);
+// The tiled GEMM addresses A rows and one group's weights with 32-bit byte offsets.
+bool tiled_offsets_fit(int64_t a_rows, int64_t lda, int64_t w_rows, int64_t K, int w_dtype);
 
 // Decode n (multiple of 8) fp8 e4m3fn codes to bf16 with the GEMM's own decoder.
 hipError_t launch_fp8_decode(const uint8_t* codes, uint16_t* out, int n, hipStream_t s);
