@@ -23,13 +23,14 @@ sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "qwen_decode"
 METRIC = "MoE-layer tokens/s; grouped-GEMM MFMA % of peak (prefill), HBM % (decode)"
-KERNEL_SOURCES = ["ffn_stream.hip", "ffn_tiled.hip"]
 
 
-def kernel_hash() -> str:
+def sources_hash(files) -> str:
+    """sha256 over the given repository files, in order: a traffic record is
+    only used while the sources of the kernel it measured are unchanged."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "sparse_mixture_experts_moe_amd", "csrc", f), "rb") as fh:
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -187,7 +188,7 @@ def main():
     tpath = os.path.join(ROOT, "profiles", f"traffic_{name}_{cfg.name}.json")
     if os.path.exists(tpath):
         tj = json.load(open(tpath))
-        if tj.get("kernel_hash") == kernel_hash():
+        if tj.get("sources") and tj.get("sources_sha256") == sources_hash(tj["sources"]):
             traffic = tj.get("bytes_per_launch")
     if ai < ridge:
         roof = {"bound": "hbm", "achieved": bytes_ / (avg_ms * 1e-3) / 1e9, "peak": cm.PEAK_HBM_GBS,
@@ -219,7 +220,7 @@ def main():
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_tokens or {"qwen_decode": 8, "ling_decode": 16}.get(cfg.name, 16)
+        n = args.cpu_sample_tokens or {"qwen_decode": 64, "ling_decode": 16}.get(cfg.name, 16)
         out["cpu_baseline"] = cpu_baseline(wl, min(n, cfg.T))
     print(json.dumps(out), flush=True)
 

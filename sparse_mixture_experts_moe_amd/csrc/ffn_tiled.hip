@@ -118,6 +118,48 @@ template <int P, int M> __device__ __forceinline__ void wait_newer(int newer) {
   }
 }
 
+// Build-time tuning knob: MOE_TILED_REMAP 1 = XCD-aware block order (measured:
+// fewer bytes fetched by the gate/up launch but more by the down projection,
+// and slower overall on the fp8 prefill; off by default).
+#ifndef MOE_TILED_REMAP
+#define MOE_TILED_REMAP 0
+#endif
+constexpr int NXCD = 8;   // XCDs; workgroup i is dispatched to XCD i % NXCD
+
+#if MOE_TILED_REMAP
+// Logical block of a physical one.  Workgroups are dispatched round-robin over
+// the XCDs, so XCD x runs blocks x, x + 8, x + 16, ...; the remap gives each
+// XCD one contiguous, equal share of the blocks that exist (the M-tiles of a
+// few experts with all their N blocks), so an expert's weight slabs and an
+// M-tile's rows are fetched into one XCD's L2 instead of all eight.
+__device__ __forceinline__ bool remap_block(const GArgs& g, int& logical) {
+  int real = 0;
+  for (int i = 0; i < g.nsets; ++i) {
+    const GSet& S = g.s[i];
+    const int m = S.tiles ? min(S.n_tiles[0], S.m_slots) : S.m_slots;
+    real += m * S.blocks_per_m * (S.ksplit > 1 ? S.ksplit : 1);
+  }
+  const int per_xcd = (real + NXCD - 1) / NXCD;
+  const int b = blockIdx.x;
+  const int slot = b / NXCD;
+  if (slot >= per_xcd) return false;
+  int l = (b % NXCD) * per_xcd + slot;
+  if (l >= real) return false;
+  // back to the grid numbering resolve_block uses (valid tiles of each set first)
+  for (int i = 0; i < g.nsets; ++i) {
+    const GSet& S = g.s[i];
+    const int m = S.tiles ? min(S.n_tiles[0], S.m_slots) : S.m_slots;
+    const int n = m * S.blocks_per_m * (S.ksplit > 1 ? S.ksplit : 1);
+    if (l < n) {
+      logical = S.block0 + l;
+      return true;
+    }
+    l -= n;
+  }
+  return false;
+}
+#endif
+
 template <class C, bool GATED, int WDT, int ODT>
 __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g) {
   constexpr bool FP8 = WDT == DT_FP8;
@@ -127,7 +169,10 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
   // select the AGPR form of the MFMAs, so the accumulators live in AGPRs and
   // the VGPRs stay free for fragments.
   asm volatile("" ::: "a0");
-  const int b = blockIdx.x;
+  int b = blockIdx.x;
+#if MOE_TILED_REMAP
+  if (!remap_block(g, b)) return;
+#endif
   int si, group, row0, row1, nblk;
   if (!resolve_block(g, b, si, group, row0, row1, nblk)) return;
   // the tile is the same for the whole block: keep it (and everything derived
@@ -340,7 +385,8 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
 
 template <class C, bool GATED, int WDT, int ODT>
 hipError_t launch_one(const GArgs& g, hipStream_t s) {
-  tiled_gemm_kernel<C, GATED, WDT, ODT><<<g.total_blocks, C::THREADS, 0, s>>>(g);
+  const int grid = MOE_TILED_REMAP ? (g.total_blocks + NXCD - 1) / NXCD * NXCD : g.total_blocks;
+  tiled_gemm_kernel<C, GATED, WDT, ODT><<<grid, C::THREADS, 0, s>>>(g);
   return hipGetLastError();
 }
 
