@@ -68,6 +68,7 @@ template <int BNW_, int WN_, int BPC_, bool FP8> struct Cfg {
   static constexpr int P = AL + BL;
   static_assert(AL * NW * 1024 == A_BYTES && BL * NW * 1024 == B_BYTES, "copy split");
   static_assert(S >= 3, "ring depth");
+  static_assert(TF == 4, "row fragments per wavefront");
 };
 
 // byte offset of 16-byte chunk c of bf16 tile row r
@@ -186,7 +187,10 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave % C::WM, wn = wave / C::WM;
+  // wavefront w runs on SIMD w % 4: rows-half wm = w / WN puts one upper-half
+  // and one lower-half wavefront of the wide block on every SIMD, so the MFMAs
+  // a short tile skips are taken off every SIMD alike
+  const int wm = wave / C::WN, wn = wave % C::WN;
   const int lr = lane & 15, q = lane >> 4;
   const int K = Sg.K;
   const int split = Sg.ksplit > 1 ? (b - Sg.block0) % Sg.ksplit : 0;
@@ -195,6 +199,8 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
   const int nst = k_len / BK;
   const int n_out = Sg.n_out;
   const int n0 = nblk * (GATED ? BNW / 2 : BNW);   // first h column (gated) / output column
+  // 16-row fragments of this wavefront that hold tile rows (the rest is padding)
+  const int na = min(TF, max(0, (row1 - row0 - wm * TF * 16 + 15) / 16));
 
   // ---- HBM -> LDS copy assignments.  Copy instruction j of a stage fills LDS
   // bytes [1024 j, 1024 j + 1024) of the A or B tile; lane l fills the 16 bytes
@@ -295,21 +301,26 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
       for (int f = 0; f < WF; ++f) F.w[f] = fp8x8_to_bf16x8(F.b[f][0], F.b[f][1]);
     }
   };
-  // MFMAs of one stage; when dst >= 0 the copies of stage dst are spread
-  // between the weight-fragment groups so their issue overlaps the MFMAs.
+  // MFMAs of one stage, row fragment by row fragment; fragments past the
+  // tile's last row (i >= na, a uniform branch) are skipped.  When dst >= 0
+  // the copies of stage dst are spread between the row-fragment groups so
+  // their issue overlaps the MFMAs.
   auto mma = [&](const Frag& F, int dst) __attribute__((always_inline)) {
-    constexpr int PER = (P + WF - 1) / WF;
+    constexpr int PER = (P + TF - 1) / TF;
 #pragma unroll
-    for (int f = 0; f < WF; ++f) {
-      bf16x8 w;
-      if constexpr (FP8) w = F.w[f];
-      else w = F.b[f];
+    for (int i = 0; i < TF; ++i) {
+      if (i < na) {
 #pragma unroll
-      for (int i = 0; i < TF; ++i)
-        acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, F.a[i], acc[f][i], 0, 0, 0);
+        for (int f = 0; f < WF; ++f) {
+          bf16x8 w;
+          if constexpr (FP8) w = F.w[f];
+          else w = F.b[f];
+          acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, F.a[i], acc[f][i], 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < PER; ++u)
-        if (f * PER + u < P && dst >= 0) issue_one(dst, f * PER + u);
+        if (i * PER + u < P && dst >= 0) issue_one(dst, i * PER + u);
     }
   };
   // One stage: stage st+1 has landed (own copies; everyone's after the
