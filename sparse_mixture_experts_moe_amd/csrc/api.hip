@@ -52,6 +52,7 @@ struct Plan {
   bool tiled;  // LDS-tiled kernel
   int mt;      // stream kernel: 16-row chunks per m-tile
   int bm;      // rows per m-tile
+  int shape;   // tiled kernel: TILED_TALL, or -1 = wide / narrow picked per launch
 };
 
 constexpr bool kTiledReady = true;
@@ -60,6 +61,10 @@ constexpr bool kTiledReady = true;
 // (build-time tuning knob).
 #ifndef MOE_MT2_MEAN
 #define MOE_MT2_MEAN 24.0
+#endif
+// Largest mean rows per group for which the tiled GEMM uses 256-row tiles.
+#ifndef MOE_TALL_MEAN
+#define MOE_TALL_MEAN 192.0
 #endif
 
 
@@ -77,39 +82,44 @@ Plan make_plan(const moe_problem_t* p, double mean_rows) {
   const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16 && tiled_fits(p);
   int policy = p->tile_policy;
   if (policy == MOE_TILE_AUTO) policy = (tiled_ok && mean_rows > 48.0) ? MOE_TILE_LDS : MOE_TILE_STREAM;
-  if (policy == MOE_TILE_LDS && tiled_ok) return Plan{true, 0, tiled_bm()};
+  if (policy == MOE_TILE_LDS && tiled_ok) {
+    // 256-row tiles read an expert's weights half as often; measured faster
+    // while groups average a few hundred rows at most, 128-row tiles beyond
+    if (mean_rows <= MOE_TALL_MEAN) return Plan{true, 0, tiled_bm(TILED_TALL), TILED_TALL};
+    return Plan{true, 0, tiled_bm(TILED_WIDE), -1};
+  }
   int mt = mean_rows <= 4.0 ? 1 : mean_rows <= MOE_MT2_MEAN ? 2 : 4;
   mt = std::min(mt, stream_max_mt(p->act_dtype));
-  return Plan{false, mt, 16 * mt};
+  return Plan{false, mt, 16 * mt, -1};
 }
 
 int routed_tile_ub(int64_t rows, int groups, int bm) {
   return static_cast<int>(std::min<int64_t>(groups, rows) + rows / bm);
 }
 
-int blocks_per_m(const Plan& pl, bool wide, bool gated, int n_out) {
-  if (pl.tiled) return tiled_blocks_n(wide, gated, n_out);
+int blocks_per_m(const Plan& pl, int shape, bool gated, int n_out) {
+  if (pl.tiled) return tiled_blocks_n(shape, gated, n_out);
   return (stream_waves_n(gated, n_out) + 3) / 4;
 }
 
-// Tiled launches use the wide block (512 weight rows) unless the narrow one
-// (256) pads the output columns of the launch's sets less.
-bool pick_wide(const GArgs& g, bool gated) {
+// Dense tiled launches (128-row tiles) use the wide block (512 weight rows)
+// unless the narrow one (256) pads the output columns of the launch's sets less.
+int pick_dense_shape(const GArgs& g, bool gated) {
   int64_t pad_w = 0, pad_n = 0;
   for (int i = 0; i < g.nsets; ++i) {
     const int n = g.s[i].n_out, ww = gated ? 256 : 512, wn = gated ? 128 : 256;
-    pad_w += static_cast<int64_t>(tiled_blocks_n(true, gated, n)) * ww - n;
-    pad_n += static_cast<int64_t>(tiled_blocks_n(false, gated, n)) * wn - n;
+    pad_w += static_cast<int64_t>(tiled_blocks_n(TILED_WIDE, gated, n)) * ww - n;
+    pad_n += static_cast<int64_t>(tiled_blocks_n(TILED_NARROW, gated, n)) * wn - n;
   }
-  return pad_w <= pad_n;
+  return pad_w <= pad_n ? TILED_WIDE : TILED_NARROW;
 }
 
 void finish_grid(GArgs& g, const Plan& pl, bool gated) {
   int b = 0;
-  g.wide = pl.tiled && pick_wide(g, gated);
+  g.shape = !pl.tiled ? -1 : pl.shape >= 0 ? pl.shape : pick_dense_shape(g, gated);
   for (int i = 0; i < g.nsets; ++i) {
     GSet& S = g.s[i];
-    S.blocks_per_m = blocks_per_m(pl, g.wide, gated, S.n_out);
+    S.blocks_per_m = blocks_per_m(pl, g.shape, gated, S.n_out);
     S.block0 = b;
     S.bm = pl.bm;
     b += S.m_slots * S.blocks_per_m * std::max(1, S.ksplit);
@@ -124,17 +134,17 @@ void finish_grid(GArgs& g, const Plan& pl, bool gated) {
 Plan router_plan(const moe_problem_t* p) {
   if (kTiledReady && p->act_dtype == MOE_BF16 && p->T >= 1024 && p->tile_policy != MOE_TILE_STREAM &&
       p->D % tiled_k_multiple() == 0 && tiled_offsets_fit(p->T, p->D, p->E, p->D, p->act_dtype))
-    return Plan{true, 0, tiled_bm()};
+    return Plan{true, 0, tiled_bm(TILED_WIDE), -1};
   int mt = p->T <= 16 ? 1 : p->T <= 32 ? 2 : 4;
   mt = std::min(mt, stream_max_mt(p->act_dtype));
-  return Plan{false, mt, 16 * mt};
+  return Plan{false, mt, 16 * mt, -1};
 }
 
 // K slices of the router: enough work items (tiled blocks or stream
 // wavefronts) to cover the GPU, each slice a multiple of 64 and >= 256 long.
 int router_splits(const moe_problem_t* p, const Plan& pl) {
   const int64_t m_tiles = (p->T + pl.bm - 1) / pl.bm;
-  const int64_t items = pl.tiled ? m_tiles * tiled_blocks_n(p->E >= 512, false, p->E)
+  const int64_t items = pl.tiled ? m_tiles * tiled_blocks_n(TILED_NARROW, false, p->E)
                                  : m_tiles * stream_waves_n(false, p->E);
   int s = 1;
   const int K = p->D;
@@ -144,7 +154,7 @@ int router_splits(const moe_problem_t* p, const Plan& pl) {
 
 hipError_t run_gemm(const GArgs& g, const Plan& pl, bool gated, int a_dt, int w_dt, int o_dt,
                     hipStream_t s) {
-  if (pl.tiled) return launch_tiled_gemm(g, g.wide != 0, gated, w_dt, o_dt, s);
+  if (pl.tiled) return launch_tiled_gemm(g, g.shape, gated, w_dt, o_dt, s);
   return launch_stream_gemm(g, pl.mt, gated, a_dt, w_dt, o_dt, s);
 }
 

@@ -6,12 +6,14 @@
 // "Ling-2.6-1T with SGLang-JAX", section 4: keep tokens and accumulators
 // resident and stream the expert weights with the next tile's fetch in flight).
 //
-// Block tile: 128 sorted rows of one group x BNW weight rows.  Two shapes are
-// built: "wide" (BNW = 512, 8 wavefronts, one block per CU) for the expert
-// FFNs and "narrow" (BNW = 256, 4 wavefronts, two blocks per CU) for narrow
-// outputs.  Either way every SIMD runs two wavefronts of 64 rows x 128 weight
-// rows (128 accumulators each, in AGPRs), which is what it takes to keep the
-// matrix cores busy; 16x16x32 bf16 MFMAs take the weight fragment as the M
+// Block tile: BM sorted rows of one group x BNW weight rows, in three shapes:
+// "tall" (256 x 256, 8 wavefronts, one block per CU) for the expert FFNs -- an
+// expert's weights are read once per 256 rows, and the row fragments a short
+// tile does not fill are skipped --, "wide" (128 x 512, 8 wavefronts) and
+// "narrow" (128 x 256, 4 wavefronts, two blocks per CU) for dense products such
+// as the router.  In all of them every SIMD runs two wavefronts of 64 rows x 128
+// weight rows (128 accumulators each, in AGPRs), which is what it takes to keep
+// the matrix cores busy; 16x16x32 bf16 MFMAs take the weight fragment as the M
 // operand, so a lane's accumulator holds 4 consecutive output columns of one
 // row.  For the fused gate/up projection the BNW weight rows are BNW/2 gate
 // rows and the matching BNW/2 up rows; each wavefront holds the gate and up
@@ -43,15 +45,15 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128;                   // rows per M-tile
 constexpr int BK = 32;                    // K elements per stage
 constexpr int ROWB = BK * 2;              // LDS bytes per bf16 tile row (64)
 constexpr int ROWB8 = BK;                 // LDS bytes per fp8 tile row (32)
 constexpr int LDS_CU = 160 * 1024;        // LDS per CU
 
-template <int BNW_, int WN_, int BPC_, bool FP8> struct Cfg {
+template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8> struct Cfg {
+  static constexpr int BM = BM_;                      // rows per M-tile
   static constexpr int BNW = BNW_;                    // weight rows per block
-  static constexpr int WM = 2, WN = WN_;              // wavefront grid (rows x weights)
+  static constexpr int WM = WM_, WN = WN_;            // wavefront grid (rows x weights)
   static constexpr int NW = WM * WN;
   static constexpr int THREADS = 64 * NW;
   static constexpr int BPC = BPC_;                    // blocks per CU
@@ -68,7 +70,7 @@ template <int BNW_, int WN_, int BPC_, bool FP8> struct Cfg {
   static constexpr int P = AL + BL;
   static_assert(AL * NW * 1024 == A_BYTES && BL * NW * 1024 == B_BYTES, "copy split");
   static_assert(S >= 3, "ring depth");
-  static_assert(TF == 4, "row fragments per wavefront");
+  static_assert(TF == 4 && WF == 8, "wavefront tile is 64 rows x 128 weight rows");
 };
 
 // byte offset of 16-byte chunk c of bf16 tile row r
@@ -187,10 +189,17 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // wavefront w runs on SIMD w % 4: rows-half wm = w / WN puts one upper-half
-  // and one lower-half wavefront of the wide block on every SIMD, so the MFMAs
-  // a short tile skips are taken off every SIMD alike
-  const int wm = wave / C::WN, wn = wave % C::WN;
+  // Wavefront w runs on SIMD w % 4.  The two wavefronts a SIMD hosts get row
+  // groups half a tile apart, so the MFMAs a short tile skips (row fragments
+  // past its last row) come off every SIMD alike.
+  int wm, wn;
+  if constexpr (C::WM == 4) {          // 8 wavefronts: 4 row groups x 2 weight groups
+    wm = (wave & 1) + 2 * (wave >> 2);
+    wn = (wave >> 1) & 1;
+  } else {                             // 2 row groups x WN weight groups
+    wm = wave / C::WN;
+    wn = wave % C::WN;
+  }
   const int lr = lane & 15, q = lane >> 4;
   const int K = Sg.K;
   const int split = Sg.ksplit > 1 ? (b - Sg.block0) % Sg.ksplit : 0;
@@ -401,10 +410,10 @@ hipError_t launch_one(const GArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BNW, int WN, int BPC>
+template <int BM, int BNW, int WM, int WN, int BPC>
 hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, hipStream_t s) {
-  using CB = Cfg<BNW, WN, BPC, false>;
-  using C8 = Cfg<BNW, WN, BPC, true>;
+  using CB = Cfg<BM, BNW, WM, WN, BPC, false>;
+  using C8 = Cfg<BM, BNW, WM, WN, BPC, true>;
   if (gated) {
     if (w_dtype == DT_BF16 && out_dtype == DT_BF16) return launch_one<CB, true, DT_BF16, DT_BF16>(g, s);
     if (w_dtype == DT_FP8 && out_dtype == DT_BF16) return launch_one<C8, true, DT_FP8, DT_BF16>(g, s);
@@ -416,16 +425,17 @@ hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, hipS
   return hipErrorInvalidValue;
 }
 
-int block_width(bool wide) { return wide ? 512 : 256; }
+// weight rows per block of a shape
+int block_width(int shape) { return shape == TILED_WIDE ? 512 : 256; }
 
 }  // namespace
 
-int tiled_bm() { return BM; }
+int tiled_bm(int shape) { return shape == TILED_TALL ? 256 : 128; }
 
 int tiled_k_multiple() { return 2 * BK; }
 
-int tiled_blocks_n(bool wide, bool gated, int n_out) {
-  const int w = gated ? block_width(wide) / 2 : block_width(wide);
+int tiled_blocks_n(int shape, bool gated, int n_out) {
+  const int w = gated ? block_width(shape) / 2 : block_width(shape);
   return (n_out + w - 1) / w;
 }
 
@@ -434,17 +444,21 @@ bool tiled_offsets_fit(int64_t a_rows, int64_t lda, int64_t w_rows, int64_t K, i
   return a_rows * lda * 2 < (int64_t(1) << 32) && w_rows * K * wb < (int64_t(1) << 32);
 }
 
-hipError_t launch_tiled_gemm(const GArgs& g, bool wide, bool gated, int w_dtype, int out_dtype,
+hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype, int out_dtype,
                              hipStream_t s) {
   if (g.total_blocks <= 0) return hipSuccess;
   for (int i = 0; i < g.nsets; ++i) {
     const GSet& S = g.s[i];
     const int ks = S.ksplit > 1 ? S.ksplit : 1;
-    if ((S.K / ks) % (2 * BK) || S.bm != BM || S.n_out % 4) return hipErrorInvalidValue;
+    if ((S.K / ks) % (2 * BK) || S.bm != tiled_bm(shape) || S.n_out % 4) return hipErrorInvalidValue;
     if (!tiled_offsets_fit(S.a_rows, S.lda, S.NB, S.K, w_dtype)) return hipErrorInvalidValue;
   }
-  return wide ? dispatch<512, 4, 1>(g, gated, w_dtype, out_dtype, s)
-              : dispatch<256, 2, 2>(g, gated, w_dtype, out_dtype, s);
+  switch (shape) {
+    case TILED_TALL: return dispatch<256, 256, 4, 2, 1>(g, gated, w_dtype, out_dtype, s);
+    case TILED_WIDE: return dispatch<128, 512, 2, 4, 1>(g, gated, w_dtype, out_dtype, s);
+    case TILED_NARROW: return dispatch<128, 256, 2, 2, 2>(g, gated, w_dtype, out_dtype, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace moe

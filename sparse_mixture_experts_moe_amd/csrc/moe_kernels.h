@@ -65,7 +65,7 @@ struct GArgs {
   GSet s[2];
   int32_t nsets;
   int32_t total_blocks;
-  int32_t wide;             // tiled kernel: 512 weight rows per block (host-side choice)
+  int32_t shape;            // tiled kernel: TILED_* block shape (host-side choice)
 };
 
 // ------------------------------------------------------------------ device helpers
@@ -161,14 +161,16 @@ hipError_t launch_stream_gemm(const GArgs& g, int mt, bool gated, int a_dtype, i
 int stream_waves_n(bool gated, int n_out);   // wave tiles along N per m-tile
 int stream_max_mt(int a_dtype);              // largest mt the stream kernel runs for a dtype
 
-// Grouped GEMM, LDS-tiled (bf16 activations, bf16 or fp8 weights), M-tiles of
-// tiled_bm() rows (every set's bm must match).  wide: 512 weight rows per block
-// (one block per CU); otherwise 256 (two blocks per CU).
-hipError_t launch_tiled_gemm(const GArgs& g, bool wide, bool gated, int w_dtype, int out_dtype,
+// Grouped GEMM, LDS-tiled (bf16 activations, bf16 or fp8 weights).  Block
+// shapes (rows x weight rows): TILED_TALL 256 x 256 (expert FFNs), TILED_WIDE
+// 128 x 512 and TILED_NARROW 128 x 256 (two blocks per CU).  Every set's bm
+// must be tiled_bm(shape).
+enum : int { TILED_TALL = 0, TILED_WIDE = 1, TILED_NARROW = 2 };
+hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype, int out_dtype,
                              hipStream_t s);
-int tiled_bm();
+int tiled_bm(int shape);
 int tiled_k_multiple();                      // every K (slice) must be a multiple of this
-int tiled_blocks_n(bool wide, bool gated, int n_out);
+int tiled_blocks_n(int shape, bool gated, int n_out);
 // The tiled GEMM addresses A rows and one group's weights with 32-bit byte offsets.
 bool tiled_offsets_fit(int64_t a_rows, int64_t lda, int64_t w_rows, int64_t K, int w_dtype);
 
