@@ -57,8 +57,11 @@ struct Plan {
 
 constexpr bool kTiledReady = true;
 
-// Largest mean rows per group for which the streamed GEMM uses 32-row tiles
-// (build-time tuning knob).
+// Largest mean rows per group for which the streamed GEMM uses 16-row /
+// 32-row tiles (build-time tuning knobs).
+#ifndef MOE_MT1_MEAN
+#define MOE_MT1_MEAN 4.0
+#endif
 #ifndef MOE_MT2_MEAN
 #define MOE_MT2_MEAN 24.0
 #endif
@@ -88,7 +91,7 @@ Plan make_plan(const moe_problem_t* p, double mean_rows) {
     if (mean_rows <= MOE_TALL_MEAN) return Plan{true, 0, tiled_bm(TILED_TALL), TILED_TALL};
     return Plan{true, 0, tiled_bm(TILED_WIDE), -1};
   }
-  int mt = mean_rows <= 4.0 ? 1 : mean_rows <= MOE_MT2_MEAN ? 2 : 4;
+  int mt = mean_rows <= MOE_MT1_MEAN ? 1 : mean_rows <= MOE_MT2_MEAN ? 2 : 4;
   mt = std::min(mt, stream_max_mt(p->act_dtype));
   return Plan{false, mt, 16 * mt, -1};
 }

@@ -32,7 +32,14 @@
 namespace moe {
 namespace {
 
-constexpr int NF = 4;            // 16-row weight fragments per wavefront
+// 16-row weight fragments per wavefront (build-time tuning knob MOE_STREAM_NF:
+// 4 or 2); a gated wavefront holds NF/2 gate and NF/2 up fragments
+#ifndef MOE_STREAM_NF
+#define MOE_STREAM_NF 4
+#endif
+constexpr int NF = MOE_STREAM_NF;
+constexpr int WROWS = 16 * NF;   // weight rows per wavefront
+static_assert(NF == 2 || NF == 4, "fragments per wavefront");
 constexpr int WAVES = 4;         // wavefronts per block (consecutive N tiles)
 
 // Build-time tuning knobs (defaults are the measured choice):
@@ -43,6 +50,10 @@ constexpr int WAVES = 4;         // wavefronts per block (consecutive N tiles)
 #endif
 #ifndef MOE_STREAM_U1
 #define MOE_STREAM_U1 2
+#endif
+//   MOE_STREAM_U2  K-steps per register stage when tiles are two 16-row chunks
+#ifndef MOE_STREAM_U2
+#define MOE_STREAM_U2 4
 #endif
 
 __device__ __forceinline__ uint4 load_w(const uint4* p) {
@@ -77,7 +88,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
   const int q = lane >> 4, lr = lane & 15;
   const int wn = nblk * WAVES + (threadIdx.x >> 6);
   const int n_out = S.n_out;
-  const int waves_n = GATED ? n_out / 32 : (n_out + 63) / 64;
+  const int waves_n = GATED ? n_out / (WROWS / 2) : (n_out + WROWS - 1) / WROWS;
   if (wn >= waves_n) return;
   const int K = S.K;
   const int nch = (row1 - row0 + 15) >> 4;  // active 16-row chunks (<= MT)
@@ -111,10 +122,10 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
   for (int f = 0; f < NF; ++f) {
     int n;
     if (GATED) {
-      n = (f < 2 ? 0 : n_out) + wn * 32 + (f & 1) * 16 + lr;
+      n = (f < NF / 2 ? 0 : n_out) + wn * (WROWS / 2) + (f % (NF / 2)) * 16 + lr;
       bv[f] = true;
     } else {
-      n = wn * 64 + f * 16 + lr;
+      n = wn * WROWS + f * 16 + lr;
       bv[f] = n < n_out;
       if (!bv[f]) n = 0;
     }
@@ -216,9 +227,9 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
       if (r >= row1) continue;
       if constexpr (GATED) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int col = wn * 32 + f * 16 + lr;
-          float gv = acc[mc][f][j], uv = acc[mc][f + 2][j];
+        for (int f = 0; f < NF / 2; ++f) {
+          const int col = wn * (WROWS / 2) + f * 16 + lr;
+          float gv = acc[mc][f][j], uv = acc[mc][f + NF / 2][j];
           if (sc) {
             gv *= sc[col];
             uv *= sc[n_out + col];
@@ -231,7 +242,7 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
       } else {
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          const int col = wn * 64 + f * 16 + lr;
+          const int col = wn * WROWS + f * 16 + lr;
           if (col >= n_out) continue;
           float v = acc[mc][f][j];
           if (sc) v *= sc[col];
@@ -254,7 +265,8 @@ template <int MT, bool GATED, int ADT, int WDT, int ODT>
 hipError_t pick_u(const GArgs& g, hipStream_t s) {
   // four-step stages when every K allows and registers do (bf16/fp8 operands,
   // at most two 16-row chunks); fp32 operands always use two-step stages
-  if constexpr (MT <= 2 && ADT != DT_F32 && !(MT == 1 && MOE_STREAM_U1 == 2)) {
+  if constexpr (MT <= 2 && ADT != DT_F32 && !(MT == 1 && MOE_STREAM_U1 == 2) &&
+                !(MT == 2 && MOE_STREAM_U2 == 2)) {
     bool k128 = true;
     for (int i = 0; i < g.nsets; ++i)
       k128 = k128 && (g.s[i].K / (g.s[i].ksplit > 1 ? g.s[i].ksplit : 1)) % 128 == 0;
@@ -304,7 +316,9 @@ hipError_t launch_fp8_decode(const uint8_t* codes, uint16_t* out, int n, hipStre
   return hipGetLastError();
 }
 
-int stream_waves_n(bool gated, int n_out) { return gated ? n_out / 32 : (n_out + 63) / 64; }
+int stream_waves_n(bool gated, int n_out) {
+  return gated ? n_out / (WROWS / 2) : (n_out + WROWS - 1) / WROWS;
+}
 
 int stream_max_mt(int a_dtype) { return a_dtype == DT_F32 ? 2 : 4; }
 
