@@ -206,9 +206,13 @@ const char* moe_status_string(moe_status_t status);
 
 /*
  * Per-stage kernel timing with HIP events, for measurement.  While enabled,
- * moe_layer records an event pair around each stage on its stream.
- * moe_timing_read waits for the recorded events, adds each stage's elapsed
- * time (ms) and launch count into ms[stage] / launches[stage] for
+ * moe_layer (and the stage entry points) record an event pair around each
+ * selected stage on their stream.  moe_timing_enable(on): on = 0 disables,
+ * on > 0 selects every stage, and on < 0 selects the stages whose bits are set
+ * in on & 0x7fffffff (bit s = stage s; e.g. (int32_t)(0x80000000u | (1u << 4))
+ * times only the gate/up projection, which keeps the events' own cost out of
+ * the other stages).  moe_timing_read waits for the recorded events, adds each stage's
+ * elapsed time (ms) and launch count into ms[stage] / launches[stage] for
  * stage < n_stages, and clears the record.  Stage names: moe_stage_name.
  * Not thread-safe; meant for a single benchmarking thread.
  */

@@ -184,8 +184,17 @@ def moe_layer(p: MoeProblem, args: MoeLayerArgs, ws, ws_bytes: int, stream=None)
            "moe_layer")
 
 
-def moe_timing_enable(on: bool):
-    _check(lib().moe_timing_enable(int(bool(on))), "moe_timing_enable")
+def moe_timing_enable(on: bool, stages=None):
+    """Enable per-stage event timing; `stages` (an iterable of stage indices)
+    restricts it to those stages."""
+    if on and stages is not None:
+        mask = 0
+        for st in stages:
+            mask |= 1 << int(st)
+        val = -(1 << 31) | (mask & 0x7FFFFFFF)
+    else:
+        val = int(bool(on))
+    _check(lib().moe_timing_enable(val), "moe_timing_enable")
 
 
 def moe_stage_count() -> int:

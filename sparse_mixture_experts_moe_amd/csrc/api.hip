@@ -65,6 +65,11 @@ constexpr bool kTiledReady = true;
 #ifndef MOE_MT2_MEAN
 #define MOE_MT2_MEAN 24.0
 #endif
+// Tiled GEMM block order: 1 = N block by N block (an expert's tiles that read
+// the same weight slab run back to back), 0 = tile by tile.
+#ifndef MOE_TILED_NMAJOR
+#define MOE_TILED_NMAJOR 0
+#endif
 // Largest mean rows per group for which the tiled GEMM uses 256-row tiles.
 #ifndef MOE_TALL_MEAN
 #define MOE_TALL_MEAN 192.0
@@ -122,6 +127,7 @@ void finish_grid(GArgs& g, const Plan& pl, bool gated) {
   g.shape = !pl.tiled ? -1 : pl.shape >= 0 ? pl.shape : pick_dense_shape(g, gated);
   for (int i = 0; i < g.nsets; ++i) {
     GSet& S = g.s[i];
+    S.nmajor = pl.tiled && MOE_TILED_NMAJOR;
     S.blocks_per_m = blocks_per_m(pl, g.shape, gated, S.n_out);
     S.block0 = b;
     S.bm = pl.bm;
@@ -171,6 +177,7 @@ struct TimingRec {
   hipEvent_t a, b;
 };
 bool g_timing = false;
+uint32_t g_timing_mask = 0xffffffffu;   // stages timed while g_timing
 std::vector<TimingRec> g_recs;
 std::vector<hipEvent_t> g_pool;
 
@@ -190,7 +197,8 @@ struct StageScope {
   hipStream_t s;
   hipEvent_t a = nullptr;
   StageScope(int st, hipStream_t st_s) : stage(st), s(st_s) {
-    if (g_timing && (a = take_event()) && hipEventRecord(a, s) != hipSuccess) {
+    if (g_timing && ((g_timing_mask >> st) & 1u) && (a = take_event()) &&
+        hipEventRecord(a, s) != hipSuccess) {
       g_pool.push_back(a);
       a = nullptr;
     }
@@ -664,6 +672,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
 // ---------------------------------------------------------------- timing ABI
 moe_status_t moe_timing_enable(int32_t on) {
   g_timing = on != 0;
+  g_timing_mask = on >= 0 ? 0xffffffffu : static_cast<uint32_t>(on) & 0x7fffffffu;
   return MOE_OK;
 }
 

@@ -47,7 +47,7 @@ struct GSet {
   int32_t NB;               // weight rows: 2*I (gated) or N (plain)
   int32_t n_out;            // output columns: I (gated) or N (plain)
   int32_t act;              // gated activation
-  int32_t pad0;
+  int32_t nmajor;           // 1: blocks ordered N block by N block (tiles fastest)
   void* out;                // output storage, row stride ldo elements
   int64_t ldo;
   const GTile* tiles;       // m-tile table, or null for dense tiles over [0, rows)
@@ -107,8 +107,14 @@ __device__ __forceinline__ bool resolve_block(const GArgs& g, int b, int& si, in
   const GSet& S = g.s[si];
   int local = b - S.block0;
   if (S.ksplit > 1) local /= S.ksplit;
-  const int m = local / S.blocks_per_m;
-  nblk = local - m * S.blocks_per_m;
+  int m;
+  if (S.nmajor) {            // consecutive blocks: same N block, consecutive tiles
+    nblk = local / S.m_slots;
+    m = local - nblk * S.m_slots;
+  } else {                   // consecutive blocks: same tile, consecutive N blocks
+    m = local / S.blocks_per_m;
+    nblk = local - m * S.blocks_per_m;
+  }
   if (S.tiles) {
     if (m >= S.n_tiles[0]) return false;
     const GTile t = S.tiles[m];

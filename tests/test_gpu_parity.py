@@ -108,6 +108,33 @@ def test_layer_edge_shapes(over):
     assert rel_err(f64(res["y"]), ref["y"]) <= tol_for(cfg)
 
 
+def test_stage_timing_mask():
+    """Timing restricted to one stage records that stage only, and the output
+    is the same as with timing off."""
+    wl = to_device(generate(SMALL["qwen_zipf"], seed=3))
+    ref = run_layer(wl)["y"].clone()
+    names = [B.moe_stage_name(i) for i in range(B.moe_stage_count())]
+    B.moe_timing_read()
+    B.moe_timing_enable(True, stages=[names.index("ffn1_gate_up_act")])
+    try:
+        y = run_layer(wl)["y"]
+        torch.cuda.synchronize()
+    finally:
+        B.moe_timing_enable(False)
+    rec = B.moe_timing_read()
+    assert rec["ffn1_gate_up_act"][1] == 1 and rec["ffn1_gate_up_act"][0] > 0
+    assert all(n == 0 for k, (_, n) in rec.items() if k != "ffn1_gate_up_act")
+    assert torch.equal(ref.view(torch.int16), y.view(torch.int16))
+    B.moe_timing_enable(True)
+    try:
+        run_layer(wl)
+        torch.cuda.synchronize()
+    finally:
+        B.moe_timing_enable(False)
+    rec = B.moe_timing_read()
+    assert rec["ffn1_gate_up_act"][1] == 1 and rec["ffn2_down"][1] == 1 and rec["combine"][1] == 1
+
+
 def test_zero_tokens_enqueues_nothing():
     cfg = shrink(CONFIGS["qwen_decode"], T=0, D=128, E=8, k=2, I=64, I_shared=64)
     p = problem(cfg)
