@@ -79,7 +79,9 @@ typedef struct moe_problem {
   int32_t I_shared;       /* shared expert / dense MLP intermediate, 0 = none */
   int32_t act;            /* MOE_ACT_* of the routed experts                 */
   int32_t act_shared;     /* MOE_ACT_* of the shared branch                  */
-  int32_t renormalize;    /* must be 1: top-k weights renormalised to sum 1  */
+  int32_t renormalize;    /* 1: top-k weights renormalised to sum 1; 0: the
+                             selected experts' softmax probabilities over all E
+                             experts ("TP MoE" page, 3.3: softmax gating) */
   int32_t act_dtype;      /* x, router weight, h, o and y: MOE_F32 | MOE_BF16 */
   int32_t w_dtype;        /* routed W13 / W2                                 */
   int32_t shared_w_dtype; /* shared W13s / W2s                               */

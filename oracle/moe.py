@@ -18,7 +18,9 @@ What it computes, step by step, in float64 with no blocking or fusion:
      all experts, then top-k, then renormalising the k probabilities ("Qwen 3.5
      MoE on Ironwood", model architecture), and equals the fused top-k-softmax
      op ("CANN Qwen3-MoE", GMM enablement and routing optimisation), because the
-     full-softmax denominator cancels.
+     full-softmax denominator cancels.  Without renormalisation (the router as
+     a linear layer plus softmax, "TP MoE" page, section 3.3) the weights are
+     the selected experts' softmax probabilities over all experts.
   3. permutation ("init routing" / "compute expert tokens" on the CANN
      Qwen3-MoE page): per-expert counts, their exclusive prefix sum, and the
      stable order of the flattened (token, slot) assignments by expert id, which
@@ -66,8 +68,14 @@ def router_logits(x: np.ndarray, wr: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- step 2
-def topk_softmax(logits: np.ndarray, k: int):
-    """float32 logits [T,E] -> (idx int32 [T,k], w float32 [T,k])."""
+def topk_softmax(logits: np.ndarray, k: int, renormalize: bool = True):
+    """float32 logits [T,E] -> (idx int32 [T,k], w float32 [T,k]).
+
+    renormalize=False keeps the selected experts' plain softmax probabilities
+    over all E experts, w_j = exp(l_j - l_0) / sum_e exp(l_e - l_0) (softmax
+    gating without renormalisation: the router is a linear layer followed by a
+    softmax, "TP MoE" page, section 3.3).
+    """
     l32 = np.asarray(logits, dtype=np.float32)
     T, E = l32.shape
     if not 1 <= k <= E:
@@ -78,7 +86,11 @@ def topk_softmax(logits: np.ndarray, k: int):
     idx = order.astype(np.int32)
     top = np.take_along_axis(l32, order, axis=1).astype(np.float64)
     ex = np.exp(top - top[:, :1])
-    w = ex / ex.sum(axis=1, keepdims=True)
+    if renormalize:
+        den = ex.sum(axis=1, keepdims=True)
+    else:
+        den = np.exp(l32.astype(np.float64) - top[:, :1]).sum(axis=1, keepdims=True)
+    w = ex / den
     return idx, w.astype(np.float32)
 
 
@@ -135,12 +147,13 @@ def shared_from_bits(w13_bits, s13, w2_bits, s2, dtype: str):
 def layer(x: np.ndarray, wr: np.ndarray, k: int, expert: ExpertFn,
           shared: Optional[tuple] = None, act: str = "silu",
           act_shared: str = "silu", logits_in: Optional[np.ndarray] = None,
-          keep: bool = False) -> dict:
+          keep: bool = False, renormalize: bool = True) -> dict:
     """The full layer on decoded float64 inputs.
 
     x [T,D], wr [E,D]; expert(e) -> (w13, s13, w2, s2) decoded; shared is the
     decoded (w13s, s13s, w2s, s2s) tuple or None.  With `logits_in` the router
-    product is skipped and the given float32 logits are routed.
+    product is skipped and the given float32 logits are routed;
+    renormalize=False gives the plain softmax weights (see topk_softmax).
     Returns y (float64) and every routing artefact; with keep=True also the
     per-row h and o (float64, sorted-row order) and the shared output.
     """
@@ -148,7 +161,7 @@ def layer(x: np.ndarray, wr: np.ndarray, k: int, expert: ExpertFn,
     T, D = x.shape
     E = wr.shape[0]
     logits = router_logits(x, wr) if logits_in is None else np.asarray(logits_in, np.float32)
-    idx, w = topk_softmax(logits, k)
+    idx, w = topk_softmax(logits, k, renormalize)
     counts, offsets, row_token, row_of_slot = permute(idx, E)
 
     o_perm = np.zeros((T * k, D), dtype=np.float64)

@@ -120,8 +120,9 @@ def status_string(status: int) -> str:
 
 
 def make_problem(T, D, E, k, I, I_shared=0, act="silu", act_shared="silu", act_dtype="bf16",
-                 w_dtype="bf16", shared_w_dtype=None, tile_policy="auto") -> MoeProblem:
-    return MoeProblem(T, D, E, k, I, I_shared, ACTS[act], ACTS[act_shared], 1,
+                 w_dtype="bf16", shared_w_dtype=None, tile_policy="auto",
+                 renormalize=True) -> MoeProblem:
+    return MoeProblem(T, D, E, k, I, I_shared, ACTS[act], ACTS[act_shared], int(bool(renormalize)),
                       DTYPES[act_dtype], DTYPES[w_dtype],
                       DTYPES[shared_w_dtype or w_dtype], POLICIES[tile_policy], 0)
 

@@ -43,7 +43,7 @@ moe_status_t check_problem(const moe_problem_t* p, bool need_ffn, bool need_rout
   if (need_ffn && !combo_ok(p->act_dtype, p->w_dtype)) return MOE_ERR_UNSUPPORTED;
   if (need_ffn && p->I_shared && !combo_ok(p->act_dtype, p->shared_w_dtype))
     return MOE_ERR_UNSUPPORTED;
-  if (p->renormalize != 1 || p->reserved != 0) return MOE_ERR_UNSUPPORTED;
+  if ((p->renormalize != 0 && p->renormalize != 1) || p->reserved != 0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -338,7 +338,8 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_rout
     MOE_LAUNCH(launch_router(p, x, w_router, logits, 1, s));
   }
   StageScope sc(ST_TOPK, s);
-  MOE_LAUNCH(launch_topk_softmax(logits, 1, nullptr, p->T, p->E, p->k, topk_idx, topk_w, s));
+  MOE_LAUNCH(launch_topk_softmax(logits, 1, nullptr, p->T, p->E, p->k, p->renormalize, topk_idx,
+                                 topk_w, s));
   return MOE_OK;
 }
 
@@ -536,7 +537,8 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
   }
   {
     StageScope sc(ST_TOPK, s);
-    MOE_LAUNCH(launch_topk_softmax(part, splits, logits_write, p->T, p->E, p->k, idx, tw, s));
+    MOE_LAUNCH(launch_topk_softmax(part, splits, logits_write, p->T, p->E, p->k, p->renormalize,
+                                   idx, tw, s));
   }
   // 2. permutation and the M-tile table (one launch for small batches)
   if (p->T <= perm_small_max_tokens() && !pl.tiled) {

@@ -136,8 +136,9 @@ __device__ __forceinline__ bool resolve_block(const GArgs& g, int b, int& si, in
 // Router logits given as `splits` partial sums part[s][T][E] (fp32), added in
 // slice order -> topk idx / weights; the summed logits are written to
 // logits_out when it is not null.
+// renorm 1: weights renormalised over the k selected; 0: plain softmax probabilities.
 hipError_t launch_topk_softmax(const float* part, int splits, float* logits_out, int T, int E,
-                               int k, int32_t* idx, float* w, hipStream_t s);
+                               int k, int renorm, int32_t* idx, float* w, hipStream_t s);
 
 // Permutation: per-block bit masks -> counts/offsets -> stable scatter.
 int perm_blocks(int T);

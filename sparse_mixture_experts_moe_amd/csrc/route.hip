@@ -1,4 +1,4 @@
-// Top-k softmax gating with renormalisation, one 64-wide wavefront per token.
+// Top-k softmax gating, one 64-wide wavefront per token.
 //
 // Selection is an exact comparison of fp32 logits: k rounds of a wavefront
 // arg-max over (value, -expert) keys, so equal values go to the lower expert
@@ -6,7 +6,9 @@
 // the softmax, w_j = exp(l_j - l_0) / sum_m exp(l_m - l_0), which is the fused
 // top-k softmax of the "CANN Qwen3-MoE" page (GMM enablement and routing
 // optimisation) and the softmax-then-top-10 router of the "Qwen 3.5 MoE on
-// Ironwood" page (model architecture) after renormalisation.
+// Ironwood" page (model architecture) after renormalisation; or, without
+// renormalisation, the selected experts' softmax probabilities over all
+// experts (the router as a linear layer plus softmax, "TP MoE" page, 3.3).
 #include "moe_kernels.h"
 
 namespace moe {
@@ -23,7 +25,7 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 template <int EPL, int TOPK_THREADS>
 __global__ __launch_bounds__(TOPK_THREADS) void topk_softmax_kernel(
     const float* __restrict__ part, int splits, float* __restrict__ logits_out, int T, int E,
-    int k, int32_t* __restrict__ idx, float* __restrict__ wout) {
+    int k, int renorm, int32_t* __restrict__ idx, float* __restrict__ wout) {
   __shared__ float lg[64 * EPL];
   const int t = blockIdx.x;
   const int64_t slice = static_cast<int64_t>(T) * E;
@@ -82,7 +84,16 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_softmax_kernel(
     }
   }
   float ex = lane < k ? expf(my_v - top_v) : 0.f;
+  // denominator: the k selected terms (renormalised), or every expert's term
+  // (plain softmax probabilities); lane partial sums in a fixed order, then a
+  // butterfly, so the result does not depend on scheduling
   float sum = ex;
+  if (!renorm) {
+    sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + 64 * j < E) sum += expf(v[j] - top_v);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
   if (lane < k) {
@@ -92,29 +103,30 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_softmax_kernel(
 }
 
 template <int EPL, int THREADS>
-void go(const float* part, int splits, float* logits_out, int T, int E, int k, int32_t* idx,
-        float* w, hipStream_t s) {
-  topk_softmax_kernel<EPL, THREADS><<<T, THREADS, 0, s>>>(part, splits, logits_out, T, E, k, idx, w);
+void go(const float* part, int splits, float* logits_out, int T, int E, int k, int renorm,
+        int32_t* idx, float* w, hipStream_t s) {
+  topk_softmax_kernel<EPL, THREADS><<<T, THREADS, 0, s>>>(part, splits, logits_out, T, E, k,
+                                                          renorm, idx, w);
 }
 
 }  // namespace
 
 hipError_t launch_topk_softmax(const float* part, int splits, float* logits_out, int T, int E,
-                               int k, int32_t* idx, float* w, hipStream_t s) {
+                               int k, int renorm, int32_t* idx, float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int epl = (E + 63) / 64;
   if (splits > 1) {
-    if (epl <= 1) go<1, 256>(part, splits, logits_out, T, E, k, idx, w, s);
-    else if (epl <= 2) go<2, 256>(part, splits, logits_out, T, E, k, idx, w, s);
-    else if (epl <= 4) go<4, 256>(part, splits, logits_out, T, E, k, idx, w, s);
-    else if (epl <= 8) go<8, 256>(part, splits, logits_out, T, E, k, idx, w, s);
-    else go<16, 256>(part, splits, logits_out, T, E, k, idx, w, s);
+    if (epl <= 1) go<1, 256>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+    else if (epl <= 2) go<2, 256>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+    else if (epl <= 4) go<4, 256>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+    else if (epl <= 8) go<8, 256>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+    else go<16, 256>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
   } else {
-    if (epl <= 1) go<1, 64>(part, splits, logits_out, T, E, k, idx, w, s);
-    else if (epl <= 2) go<2, 64>(part, splits, logits_out, T, E, k, idx, w, s);
-    else if (epl <= 4) go<4, 64>(part, splits, logits_out, T, E, k, idx, w, s);
-    else if (epl <= 8) go<8, 64>(part, splits, logits_out, T, E, k, idx, w, s);
-    else go<16, 64>(part, splits, logits_out, T, E, k, idx, w, s);
+    if (epl <= 1) go<1, 64>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+    else if (epl <= 2) go<2, 64>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+    else if (epl <= 4) go<4, 64>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+    else if (epl <= 8) go<8, 64>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+    else go<16, 64>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
   }
   return hipGetLastError();
 }

@@ -65,7 +65,8 @@ def _ok_problem(**over):
     (dict(tile_policy=5), B.MOE_ERR_DTYPE),
     (dict(w_dtype=B.MOE_BF16), B.MOE_ERR_UNSUPPORTED),              # f32 act x bf16 weights
     (dict(act_dtype=B.MOE_FP8_E4M3FN), B.MOE_ERR_UNSUPPORTED),
-    (dict(renormalize=0), B.MOE_ERR_UNSUPPORTED), (dict(reserved=1), B.MOE_ERR_UNSUPPORTED),
+    (dict(renormalize=2), B.MOE_ERR_UNSUPPORTED), (dict(reserved=1), B.MOE_ERR_UNSUPPORTED),
+    (dict(renormalize=0), B.MOE_OK),
 ])
 def test_validation_codes(lib, over, status):
     p = _ok_problem(**over)

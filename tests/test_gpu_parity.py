@@ -108,6 +108,40 @@ def test_layer_edge_shapes(over):
     assert rel_err(f64(res["y"]), ref["y"]) <= tol_for(cfg)
 
 
+# fp32 plain-softmax weight: expf (2 ulp) of each term, a sum of E/64 terms per
+# lane then 6 butterfly levels, and a divide: under 25 ulp (1.5e-6) for E <= 1024
+PLAIN_W_RTOL = 3e-6
+
+
+@pytest.mark.parametrize("policy", ["stream", "lds"])
+@pytest.mark.parametrize("name", ["qwen_ragged", "ling_fp8", "big_groups_bf16"])
+def test_layer_plain_softmax_gating(name, policy):
+    """renormalize = 0: routing with oracle logits is bit-exact, the weights are
+    the plain softmax probabilities, and the layer is within tolerance."""
+    cfg = SMALL[name]
+    wl = to_device(generate(cfg, seed=8))
+    ref = oracle_layer(wl, renormalize=False)
+    res = run_layer(wl, policy, logits_in=torch.from_numpy(ref["logits"]).cuda(), renormalize=False)
+    _check_routing(res, ref, w_rtol=PLAIN_W_RTOL)
+    assert np.all(ref["w"].sum(axis=1) < 1.0)
+    assert rel_err(f64(res["y"]), ref["y"]) <= tol_for(cfg)
+
+
+@pytest.mark.parametrize("T,E,k", [(300, 96, 6), (129, 1024, 32), (64, 8, 8)])
+def test_moe_route_plain_softmax(T, E, k):
+    l = np.random.default_rng(9).standard_normal((T, E)).astype(np.float32) * 2
+    cfg = shrink(CONFIGS["qwen_decode"], T=T, D=128, E=E, k=k, I=64, I_shared=64)
+    p = problem(cfg, renormalize=False)
+    logits = torch.from_numpy(l).cuda()
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    B.moe_route(p, None, None, logits, True, idx, w)
+    torch.cuda.synchronize()
+    ri, rw = topk_softmax(l, k, renormalize=False)
+    assert np.array_equal(idx.cpu().numpy(), ri)
+    assert np.allclose(w.cpu().numpy(), rw, rtol=PLAIN_W_RTOL, atol=0)
+
+
 def test_stage_timing_mask():
     """Timing restricted to one stage records that stage only, and the output
     is the same as with timing off."""

@@ -102,3 +102,37 @@ def test_router_logits_against_exact_sums():
         for e in range(16):
             exact = np.float32(math.fsum(float(a) * float(b) for a, b in zip(x[t], wr[e])))
             assert abs(float(l[t, e]) - float(exact)) <= float(np.spacing(np.abs(exact)))
+
+
+# ---------------------------------------------------------------- softmax gating without renormalisation
+def test_plain_softmax_weights_match_library_softmax():
+    """renormalize=False: the weights are scipy's softmax over all experts,
+    read at the selected indices."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(11)
+    l = (rng.standard_normal((50, 40)) * 3).astype(np.float32)
+    idx, w = topk_softmax(l, 6, renormalize=False)
+    ref = softmax(l.astype(np.float64), axis=1)
+    assert np.allclose(w, np.take_along_axis(ref, idx.astype(np.int64), axis=1), rtol=1e-6, atol=0)
+    assert np.array_equal(idx, topk_softmax(l, 6)[0])          # selection is unchanged
+    assert np.all(w.sum(axis=1) < 1.0) and np.all(np.diff(w, axis=1) <= 0)
+
+
+def test_plain_and_renormalised_agree_when_every_expert_is_selected():
+    """k = E: both are the full softmax."""
+    l = _planted(20, 9, seed=3)
+    _, wr = topk_softmax(l, 9)
+    _, wp = topk_softmax(l, 9, renormalize=False)
+    assert np.allclose(wr, wp, rtol=1e-6, atol=0)
+
+
+def test_plain_weights_are_renormalised_weights_times_selected_mass():
+    """w_plain = w_renorm * (selected softmax mass), a closed form."""
+    rng = np.random.default_rng(5)
+    l = rng.standard_normal((30, 24)).astype(np.float32)
+    idx, wr = topk_softmax(l, 4)
+    _, wp = topk_softmax(l, 4, renormalize=False)
+    l64 = l.astype(np.float64)
+    mass = np.exp(np.take_along_axis(l64, idx.astype(np.int64), axis=1) - l64.max(axis=1, keepdims=True)).sum(axis=1) \
+        / np.exp(l64 - l64.max(axis=1, keepdims=True)).sum(axis=1)
+    assert np.allclose(wp, wr * mass[:, None], rtol=2e-6, atol=0)
