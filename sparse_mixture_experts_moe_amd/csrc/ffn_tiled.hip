@@ -20,24 +20,31 @@
 // halves of the same 64 h columns and forms act(gate)*up in registers (the
 // packed gate/up tile of GMM v2 on the Ironwood page).
 //
-// K is staged 32 elements at a time through a ring of S LDS buffers filled by
+// K is staged BK elements at a time through a ring of S LDS buffers filled by
 // direct HBM -> LDS loads (global_load_lds_dwordx4: a lane's 16 bytes land at
 // the instruction's LDS base + 16 x lane).  Stage st+S is fetched while stage
-// st is multiplied, and a wavefront's fragments for stage st+1 are read from
-// LDS while its MFMAs of stage st run, so neither the fetch latency nor the
-// LDS latency sits in front of the matrix cores; the copies of a stage are
-// spread between the MFMA groups.  One barrier per stage publishes a stage's
-// copies and frees the slot that was read before.
+// st is multiplied, and a wavefront's fragments for the next 32-deep sub-step
+// are read from LDS while its MFMAs of the current one run, so neither the
+// fetch latency nor the LDS latency sits in front of the matrix cores; the
+// copies of a stage are spread between the MFMA groups.  One barrier per stage
+// publishes a stage's copies and frees the slot that was read before.
 //
-// LDS rows hold 32 bf16 (64 bytes, 4 chunks of 16); chunk c of row r sits at
-// c ^ ((r >> 1) & 3), which keeps the fragment reads free of bank conflicts.
-// Since a copy lane's LDS position is fixed by its lane index, the swizzle is
-// applied on the source side: the lane that fills a position fetches the
-// chunk that belongs there.  fp8 e4m3fn weights stay fp8 in LDS (32-byte rows
-// of two 16-byte halves, half h of row r at h ^ ((r >> 3) & 1)) and are decoded
-// exactly to bf16 when a stage's fragments are taken up, which halves the
-// weight tile's LDS footprint; per-channel scales are applied after the
-// reduction.
+// Each copy fetches BK contiguous elements of a row, and the L2 serves one
+// request per row segment whatever its length, so with fp8 weights (32-byte
+// segments at BK = 32) the GEMM is bound by the L2's request rate before the
+// matrix cores; fp8 weights are therefore staged 64 deep (64-byte weight and
+// 128-byte activation segments, half the requests per FLOP).  bf16 tiles stay
+// 32 deep, where a deeper stage would leave fewer than three in the LDS ring.
+//
+// A tile row of RB bytes holds RB / 16 chunks of 16 bytes; chunk c of row r
+// sits at a position XORed with a few bits of r (upos below), chosen so that
+// the rows sharing a 256-byte line of the 64 banks, and the rows one fragment
+// read serves per cycle, fall on distinct banks.  Since a copy lane's LDS
+// position is fixed by its lane index, the swizzle is applied on the source
+// side: the lane that fills a position fetches the chunk that belongs there.
+// fp8 e4m3fn weights stay fp8 in LDS and are decoded exactly to bf16 when a
+// sub-step's fragments are taken up, which halves the weight tile's LDS
+// footprint; per-channel scales are applied after the reduction.
 #include <type_traits>
 
 #include "moe_kernels.h"
@@ -45,12 +52,14 @@
 namespace moe {
 namespace {
 
-constexpr int BK = 32;                    // K elements per stage
-constexpr int ROWB = BK * 2;              // LDS bytes per bf16 tile row (64)
-constexpr int ROWB8 = BK;                 // LDS bytes per fp8 tile row (32)
+constexpr int KS = 32;                    // K elements per MFMA sub-step
 constexpr int LDS_CU = 160 * 1024;        // LDS per CU
 
-template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8> struct Cfg {
+template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8, int BK_> struct Cfg {
+  static constexpr int BK = BK_;                      // K elements per stage
+  static constexpr int H = BK / KS;                   // sub-steps per stage
+  static constexpr int ROWB = BK * 2;                 // LDS bytes per bf16 tile row
+  static constexpr int ROWB8 = BK;                    // LDS bytes per fp8 tile row
   static constexpr int BM = BM_;                      // rows per M-tile
   static constexpr int BNW = BNW_;                    // weight rows per block
   static constexpr int WM = WM_, WN = WN_;            // wavefront grid (rows x weights)
@@ -68,17 +77,20 @@ template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8> struct Cfg {
   static constexpr int AL = A_BYTES / 1024 / NW;      // 1 KiB copy instructions per wavefront, A
   static constexpr int BL = B_BYTES / 1024 / NW;      // same, B
   static constexpr int P = AL + BL;
+  static constexpr int P1 = (P + H - 1) / H;          // copies issued in a stage's first sub-step
   static_assert(AL * NW * 1024 == A_BYTES && BL * NW * 1024 == B_BYTES, "copy split");
+  static_assert(H == 1 || H == 2, "stage depth");
   static_assert(S >= 3, "ring depth");
   static_assert(TF == 4 && WF == 8, "wavefront tile is 64 rows x 128 weight rows");
 };
 
-// byte offset of 16-byte chunk c of bf16 tile row r
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * ROWB + ((chunk ^ ((row >> 1) & 3)) << 4);
+// position of 16-byte chunk c in a tile row of RB bytes (an involution in c):
+// 256 / RB rows share a line of the 64 banks, and consecutive groups of them
+// XOR the chunk index with consecutive values
+template <int RB> __device__ __forceinline__ int upos(int row, int c) {
+  constexpr int SH = RB == 32 ? 3 : RB == 64 ? 2 : 1;
+  return c ^ ((row >> SH) & (RB / 16 - 1));
 }
-// 16-byte half of fp8 tile row r that holds logical half h (an involution)
-__device__ __forceinline__ int half8(int row, int h) { return h ^ ((row >> 3) & 1); }
 
 // HBM -> LDS copy of 16 bytes per lane from sbase + voff to lds + 16 * lane;
 // sbase and lds are wave-uniform.  Issued through inline asm so the compiler
@@ -167,6 +179,7 @@ template <class C, bool GATED, int WDT, int ODT>
 __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g) {
   constexpr bool FP8 = WDT == DT_FP8;
   constexpr int TF = C::TF, WF = C::WF, S = C::S, P = C::P, BNW = C::BNW;
+  constexpr int H = C::H, ROWB = C::ROWB, ROWB8 = C::ROWB8;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   // An (empty) statement that names an accumulation register makes the backend
   // select the AGPR form of the MFMAs, so the accumulators live in AGPRs and
@@ -205,7 +218,7 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
   const int split = Sg.ksplit > 1 ? (b - Sg.block0) % Sg.ksplit : 0;
   const int k_len = Sg.ksplit > 1 ? K / Sg.ksplit : K;
   const int k_beg = split * k_len;
-  const int nst = k_len / BK;
+  const int nst = k_len / C::BK;
   const int n_out = Sg.n_out;
   const int n0 = nblk * (GATED ? BNW / 2 : BNW);   // first h column (gated) / output column
   // 16-row fragments of this wavefront that hold tile rows (the rest is padding)
@@ -222,8 +235,9 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
 #pragma unroll
   for (int i = 0; i < C::AL; ++i) {
     const int j = wave * C::AL + i;
-    const int tr = 16 * j + (lane >> 2);             // 4 lanes per 64-byte row
-    const int c = (lane & 3) ^ ((tr >> 1) & 3);      // logical chunk of this position
+    constexpr int LPR = ROWB / 16;                    // lanes per row
+    const int tr = (64 / LPR) * j + lane / LPR;
+    const int c = upos<ROWB>(tr, lane % LPR);        // logical chunk of this position
     const int r = row0 + tr;
     int64_t arow = 0;
     if (r < row1) {
@@ -238,8 +252,9 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
 #pragma unroll
   for (int i = 0; i < C::BL; ++i) {
     const int j = wave * C::BL + i;
-    // bf16: 4 lanes per 64-byte row; fp8: 2 lanes per 32-byte row
-    const int tr = FP8 ? 32 * j + (lane >> 1) : 16 * j + (lane >> 2);
+    constexpr int RB = FP8 ? ROWB8 : ROWB, LPR = RB / 16;
+    const int tr = (64 / LPR) * j + lane / LPR;
+    const int c = upos<RB>(tr, lane % LPR);
     int wrow;
     if (GATED) {
       const int n = n0 + (tr & (BNW / 2 - 1));
@@ -247,18 +262,16 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
     } else {
       wrow = n0 + tr < n_out ? n0 + tr : 0;
     }
-    b_off[i] = FP8 ? static_cast<uint32_t>(static_cast<int64_t>(wrow) * K + half8(tr, lane & 1) * 16)
-                   : static_cast<uint32_t>((static_cast<int64_t>(wrow) * K +
-                                            ((lane & 3) ^ ((tr >> 1) & 3)) * 8) * 2);
+    b_off[i] = static_cast<uint32_t>((static_cast<int64_t>(wrow) * K * (FP8 ? 1 : 2)) + c * 16);
   }
   // copy instruction k (0..P-1) of stage st: the A instructions, then B
   auto issue_one = [&](int st, int k) __attribute__((always_inline)) {
     char* base = smem + (st % S) * C::STAGE;
     if (k < C::AL) {
-      dma16(a_off[k], a_base + st * (BK * 2), base + (wave * C::AL + k) * 1024);
+      dma16(a_off[k], a_base + st * ROWB, base + (wave * C::AL + k) * 1024);
     } else {
       const int i = k - C::AL;
-      dma16(b_off[i], b_base + st * (FP8 ? BK : BK * 2),
+      dma16(b_off[i], b_base + st * (FP8 ? ROWB8 : ROWB),
             base + C::A_BYTES + (wave * C::BL + i) * 1024);
     }
   };
@@ -283,19 +296,25 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
     BT b[WF];
     bf16x8 w[FP8 ? WF : 1];
   };
-  auto readf = [&](Frag& F, int st) __attribute__((always_inline)) {
-    const char* base = smem + (st % S) * C::STAGE;
+  // fragments of sub-step t (K elements [32 t, 32 t + 32) of the tile): lane
+  // (lr, q) takes K elements 8q..8q+7 of the sub-step
+  auto readf = [&](Frag& F, int t) __attribute__((always_inline)) {
+    const int h = t % H;
+    const char* base = smem + ((t / H) % S) * C::STAGE;
     const char* bb = base + C::A_BYTES;
 #pragma unroll
-    for (int i = 0; i < TF; ++i)
-      F.a[i] = *reinterpret_cast<const bf16x8*>(base + swz(wm * TF * 16 + 16 * i + lr, q));
+    for (int i = 0; i < TF; ++i) {
+      const int r = wm * TF * 16 + 16 * i + lr;
+      F.a[i] = *reinterpret_cast<const bf16x8*>(base + r * ROWB + upos<ROWB>(r, 4 * h + q) * 16);
+    }
 #pragma unroll
     for (int f = 0; f < WF; ++f) {
       const int tr = wrow_of(f);
       if constexpr (FP8)
-        F.b[f] = *reinterpret_cast<const u32x2*>(bb + tr * ROWB8 + half8(tr, q >> 1) * 16 + (q & 1) * 8);
+        F.b[f] = *reinterpret_cast<const u32x2*>(bb + tr * ROWB8 + upos<ROWB8>(tr, 2 * h + (q >> 1)) * 16 +
+                                                 (q & 1) * 8);
       else
-        F.b[f] = *reinterpret_cast<const bf16x8*>(bb + swz(tr, q));
+        F.b[f] = *reinterpret_cast<const bf16x8*>(bb + tr * ROWB + upos<ROWB>(tr, 4 * h + q) * 16);
     }
   };
   // Use the fragments in an empty statement so that the compiler's own wait
@@ -310,12 +329,13 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
       for (int f = 0; f < WF; ++f) F.w[f] = fp8x8_to_bf16x8(F.b[f][0], F.b[f][1]);
     }
   };
-  // MFMAs of one stage, row fragment by row fragment; fragments past the
-  // tile's last row (i >= na, a uniform branch) are skipped.  When dst >= 0
-  // the copies of stage dst are spread between the row-fragment groups so
+  // MFMAs of one sub-step, row fragment by row fragment; fragments past the
+  // tile's last row (i >= na, a uniform branch) are skipped.  When dst >= 0,
+  // copies K0..K1-1 of stage dst are spread between the row-fragment groups so
   // their issue overlaps the MFMAs.
-  auto mma = [&](const Frag& F, int dst) __attribute__((always_inline)) {
-    constexpr int PER = (P + TF - 1) / TF;
+  auto mma = [&](const Frag& F, int dst, auto k0, auto k1) __attribute__((always_inline)) {
+    constexpr int K0 = decltype(k0)::value, NK = decltype(k1)::value - K0;
+    constexpr int PER = (NK + TF - 1) / TF;
 #pragma unroll
     for (int i = 0; i < TF; ++i) {
       if (i < na) {
@@ -329,19 +349,33 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
       }
 #pragma unroll
       for (int u = 0; u < PER; ++u)
-        if (i * PER + u < P && dst >= 0) issue_one(dst, i * PER + u);
+        if (i * PER + u < NK && dst >= 0) issue_one(dst, K0 + i * PER + u);
     }
   };
-  // One stage: stage st+1 has landed (own copies; everyone's after the
-  // barrier, which also frees slot st % S for stage st+S); st+1's fragments
-  // are read while st's MFMAs run.
-  auto step = [&](Frag& cur, Frag& nxt, int st) __attribute__((always_inline)) {
-    wait_newer<P, S - 2>(max(0, min(S - 2, nst - 2 - st)));
-    settle(cur);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    readf(nxt, st + 1);          // st + 1 == nst reads a stale slot that is never used
-    mma(cur, st + S < nst ? st + S : -1);
+  using I0 = std::integral_constant<int, 0>;
+  using IP1 = std::integral_constant<int, C::P1>;
+  using IP = std::integral_constant<int, P>;
+  // Sub-step t.  When sub-step t + 1 opens a stage, that stage has landed
+  // (own copies; everyone's after the barrier, which also frees the slot of
+  // the stage just finished for the stage S further on, whose copies go out
+  // during this sub-step and, with two sub-steps per stage, the next one).
+  // Sub-step t + 1's fragments are read while t's MFMAs run.
+  auto step = [&](Frag& cur, Frag& nxt, int t, auto odd) __attribute__((always_inline)) {
+    constexpr bool OPENS = H == 1 || decltype(odd)::value;   // t + 1 opens a stage
+    if constexpr (OPENS) {
+      const int x = (t + 1) / H - 1;   // the stage finished by this sub-step
+      wait_newer<P, S - 2>(max(0, min(S - 2, nst - 2 - x)));
+      settle(cur);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      readf(nxt, t + 1);   // t + 1 == nst * H reads a stale slot that is never used
+      mma(cur, x + S < nst ? x + S : -1, I0(), IP1());
+    } else {
+      const int x = t / H - 1;         // its slot was freed by the last barrier
+      settle(cur);                     // (decodes fp8 weights)
+      readf(nxt, t + 1);
+      mma(cur, x >= 0 && x + S < nst ? x + S : -1, IP1(), IP());
+    }
   };
 
   // ---- prologue: S stages in flight, stage 0's fragments read
@@ -355,9 +389,11 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   readf(F0, 0);
-  for (int st = 0; st < nst; st += 2) {   // nst is even (checked by the launcher)
-    step(F0, F1, st);
-    step(F1, F0, st + 1);
+  // nst * H sub-steps, an even number (with one sub-step per stage, nst is
+  // even: checked by the launcher)
+  for (int t = 0; t < nst * H; t += 2) {
+    step(F0, F1, t, std::false_type());
+    step(F1, F0, t + 1, std::true_type());
   }
   wait_vm<0>();   // no copy may still be in flight when the block retires
 
@@ -412,8 +448,9 @@ hipError_t launch_one(const GArgs& g, hipStream_t s) {
 
 template <int BM, int BNW, int WM, int WN, int BPC>
 hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, hipStream_t s) {
-  using CB = Cfg<BM, BNW, WM, WN, BPC, false>;
-  using C8 = Cfg<BM, BNW, WM, WN, BPC, true>;
+  using CB = Cfg<BM, BNW, WM, WN, BPC, false, 32>;
+  // fp8 weights 64 deep where three such stages fit in the block's LDS share
+  using C8 = Cfg<BM, BNW, WM, WN, BPC, true, (BPC == 1 ? 64 : 32)>;
   if (gated) {
     if (w_dtype == DT_BF16 && out_dtype == DT_BF16) return launch_one<CB, true, DT_BF16, DT_BF16>(g, s);
     if (w_dtype == DT_FP8 && out_dtype == DT_BF16) return launch_one<C8, true, DT_FP8, DT_BF16>(g, s);
@@ -432,7 +469,7 @@ int block_width(int shape) { return shape == TILED_WIDE ? 512 : 256; }
 
 int tiled_bm(int shape) { return shape == TILED_TALL ? 256 : 128; }
 
-int tiled_k_multiple() { return 2 * BK; }
+int tiled_k_multiple() { return 2 * KS; }
 
 int tiled_blocks_n(int shape, bool gated, int n_out) {
   const int w = gated ? block_width(shape) / 2 : block_width(shape);
@@ -450,7 +487,7 @@ hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype,
   for (int i = 0; i < g.nsets; ++i) {
     const GSet& S = g.s[i];
     const int ks = S.ksplit > 1 ? S.ksplit : 1;
-    if ((S.K / ks) % (2 * BK) || S.bm != tiled_bm(shape) || S.n_out % 4) return hipErrorInvalidValue;
+    if ((S.K / ks) % (2 * KS) || S.bm != tiled_bm(shape) || S.n_out % 4) return hipErrorInvalidValue;
     if (!tiled_offsets_fit(S.a_rows, S.lda, S.NB, S.K, w_dtype)) return hipErrorInvalidValue;
   }
   switch (shape) {
