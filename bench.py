@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--policy", default="auto", choices=["auto", "stream", "lds"])
+    ap.add_argument("--act-quant", action="store_true",
+                    help="dynamic per-token fp8 activations in the expert GEMMs (fp8-weight workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -69,7 +71,7 @@ def copy_calib(mib: int):
     print(json.dumps({"copy_calib_bytes": n, "copies": 10}), flush=True)
 
 
-def cpu_baseline(wl, n_tokens: int):
+def cpu_baseline(wl, n_tokens: int, act_quant: bool = False):
     """Time the oracle (as it stands) on the first n_tokens tokens of the batch:
     routing of those tokens, every expert they touch, the shared branch and
     the combine, with expert weights decoded from their stored format inside
@@ -77,6 +79,7 @@ def cpu_baseline(wl, n_tokens: int):
     import numpy as np
     from threadpoolctl import threadpool_info
 
+    from oracle.actquant import layer_w8a8
     from oracle.formats import decode
     from oracle.moe import layer
     from workloads import host_expert, host_shared, to_bits
@@ -103,14 +106,15 @@ def cpu_baseline(wl, n_tokens: int):
     shared = None
     if sh is not None:
         shared = (decode(sh[0], c.shared_w_dtype), sh[1], decode(sh[2], c.shared_w_dtype), sh[3])
-    layer(x, wr, c.k, expert, shared, c.act, c.act_shared)
+    (layer_w8a8 if act_quant else layer)(x, wr, c.k, expert, shared, c.act, c.act_shared)
     dt = time.perf_counter() - t0
     threads = 1
     for info in threadpool_info():
         if info.get("user_api") == "blas":
             threads = max(threads, int(info.get("num_threads", 1)))
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"float64 NumPy oracle, whole layer on the first {n_tokens} of {c.T} tokens "
+            "sample": (f"float64 NumPy oracle{' (W8A8)' if act_quant else ''}, whole layer on the "
+                       f"first {n_tokens} of {c.T} tokens "
                        f"({len(used)} experts decoded from {c.w_dtype}), {dt:.1f} s")}
 
 
@@ -137,7 +141,8 @@ def main():
     wl = generate(cfg, seed=0, weight_device="cuda")
     wl.x, wl.wr = wl.x.cuda(), wl.wr.cuda()
     p = B.make_problem(cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.act, cfg.act_shared,
-                       cfg.act_dtype, cfg.w_dtype, cfg.shared_w_dtype, args.policy)
+                       cfg.act_dtype, cfg.w_dtype, cfg.shared_w_dtype, args.policy,
+                       act_quant=B.MOE_ACT_QUANT_FP8_ROW if args.act_quant else 0)
     ws_bytes = B.moe_layer_workspace_size(p)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     y = torch.empty((cfg.T, cfg.D), dtype=wl.x.dtype, device="cuda")
@@ -200,10 +205,12 @@ def main():
     bytes_ /= launches_per_step
     flops /= launches_per_step
     ai = flops / bytes_ if bytes_ else 0.0
-    wdt = "bf16" if cfg.act_dtype == "bf16" else "f32"
+    # the matrix cores' dtype: fp8 x fp8 with quantised activations
+    wdt = "fp8" if args.act_quant else ("bf16" if cfg.act_dtype == "bf16" else "f32")
     ridge = cm.PEAK_TFLOPS[wdt] * 1e12 / (cm.PEAK_HBM_GBS * 1e9)
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", f"traffic_{name}_{cfg.name}.json")
+    tpath = os.path.join(ROOT, "profiles",
+                         f"traffic_{name}_{cfg.name}{'_w8a8' if args.act_quant else ''}.json")
     if os.path.exists(tpath):
         tj = json.load(open(tpath))
         if tj.get("sources") and tj.get("sources_sha256") == sources_hash(tj["sources"]):
@@ -224,14 +231,16 @@ def main():
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if cfg.act_dtype == "bf16" else "f32", "data": "synthetic",
+        "dtype": wdt, "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "D": cfg.D, "E": cfg.E, "k": cfg.k,
                    "I": cfg.I, "I_shared": cfg.I_shared, "act": cfg.act,
-                   "w_dtype": cfg.w_dtype, "touched_experts": touched, "policy": args.policy},
+                   "w_dtype": cfg.w_dtype, "touched_experts": touched, "policy": args.policy,
+                   "act_quant": "fp8_per_token" if args.act_quant else "none"},
         "roofline": roof,
         "grouped_gemm": {
             "ms_per_step": gemm_ms,
             "mfma_frac_bf16": cm.gemm_flops(cfg) / (gemm_ms * 1e-3) / (cm.PEAK_TFLOPS["bf16"] * 1e12),
+            "mfma_frac_fp8": cm.gemm_flops(cfg) / (gemm_ms * 1e-3) / (cm.PEAK_TFLOPS["fp8"] * 1e12),
             "hbm_frac_layer_bytes": cm.layer_bytes(cfg, touched) / (ms_per_step * 1e-3)
             / (cm.PEAK_HBM_GBS * 1e9)},
         "stages_ms_per_step": {k: v[0] / diag_steps for k, v in diag.items()},
@@ -239,7 +248,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         n = args.cpu_sample_tokens or {"qwen_decode": 64, "ling_decode": 16}.get(cfg.name, 16)
-        out["cpu_baseline"] = cpu_baseline(wl, min(n, cfg.T))
+        out["cpu_baseline"] = cpu_baseline(wl, min(n, cfg.T), args.act_quant)
     print(json.dumps(out), flush=True)
 
 

@@ -30,7 +30,8 @@
  *    channel scales s13[e][2I] and s2[e][D], applied after the reduction
  *    ("Ling-2.6-1T with SGLang-JAX" page, section 5, per-channel scaling).
  *  - Supported dtype combinations: {act F32, weights F32} and
- *    {act BF16, weights BF16 or FP8_E4M3FN}; anything else is
+ *    {act BF16, weights BF16 or FP8_E4M3FN}, the latter also with dynamic
+ *    per-token fp8 activations (act_quant); anything else is
  *    MOE_ERR_UNSUPPORTED (no silent fallback).
  *  - Limits: 1 <= k <= min(E, 32); E <= 1024; D, I, I_shared multiples of 64;
  *    T*k and T*max(D, I) below 2^31.  T == 0 is valid and enqueues nothing.
@@ -59,6 +60,10 @@ extern "C" {
 #define MOE_TILE_STREAM   1    /* register-streamed weights, small groups  */
 #define MOE_TILE_LDS      2    /* LDS-tiled MFMA GEMM, large groups         */
 
+/* activation quantisation of the expert GEMMs (moe_problem_t.act_quant) */
+#define MOE_ACT_QUANT_NONE     0   /* bf16 activations                       */
+#define MOE_ACT_QUANT_FP8_ROW  1   /* dynamic per-token fp8 (see below)      */
+
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_NULL = 1,          /* a required pointer is NULL               */
@@ -86,8 +91,27 @@ typedef struct moe_problem {
   int32_t w_dtype;        /* routed W13 / W2                                 */
   int32_t shared_w_dtype; /* shared W13s / W2s                               */
   int32_t tile_policy;    /* MOE_TILE_*                                      */
-  int32_t reserved;       /* must be 0                                       */
+  int32_t act_quant;      /* MOE_ACT_QUANT_*: activations of the expert GEMMs */
 } moe_problem_t;
+
+/*
+ * act_quant (grouped FFN and fused layer):
+ *  MOE_ACT_QUANT_NONE     bf16 activations (weights decoded exactly; W8A16
+ *                         with fp8 weights).
+ *  MOE_ACT_QUANT_FP8_ROW  dynamic per-token fp8 activations, the activation
+ *                         quantisation of the "Ling-2.6-1T with SGLang-JAX"
+ *                         page, section 5: each GEMM input row (x for the
+ *                         gate/up projection, the stored bf16 h for the down
+ *                         projection) is quantised as moe_quantize_rows does,
+ *                         multiplied with the fp8 weights on the fp8 matrix
+ *                         cores (fp32 sums), and scaled per row and per output
+ *                         channel after the reduction.  Requires act BF16,
+ *                         fp8 routed (and shared) weights, D, I and I_shared
+ *                         multiples of 128 and a tile policy other than
+ *                         MOE_TILE_STREAM; routing and combine are unchanged.
+ *                         Results differ from the exact layer by the
+ *                         quantisation (a few per cent of the output range).
+ */
 
 /*
  * moe_route -- router logits and top-k softmax gating.
@@ -148,6 +172,9 @@ moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_
  *   out [rows_upper_bound, D] act dtype (written)
  *   rows_upper_bound  host-known bound on offsets[n_groups]; it sizes the grid
  *   ws / ws_bytes     scratch of at least moe_grouped_ffn_workspace_size bytes
+ *   With act_quant = MOE_ACT_QUANT_FP8_ROW the quantised copies of the A rows
+ *   and of h (and their scales) live in the workspace; h is still written in
+ *   bf16 (it is the stored value that gets quantised).
  */
 moe_status_t moe_grouped_ffn_workspace_size(const moe_problem_t* p, int32_t n_groups,
                                             int32_t rows_upper_bound, size_t* bytes);
@@ -196,12 +223,29 @@ typedef struct moe_layer_args {
  * moe_layer -- the whole layer, every step enqueued on one stream with no
  * host synchronisation: route -> permute -> grouped FFN (routed experts and the
  * shared branch in the same launches) -> combine.  The workspace holds every
- * intermediate (logits, routing metadata, h, o); its size depends only on the
+ * intermediate (logits, routing metadata, h, o, and with act_quant the fp8
+ * copies of x and h with their row scales); its size depends only on the
  * problem.
  */
 moe_status_t moe_layer_workspace_size(const moe_problem_t* p, size_t* bytes);
 moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* args, void* ws,
                        size_t ws_bytes, void* stream);
+
+/*
+ * moe_quantize_rows -- dynamic per-row fp8 quantisation ("Ling-2.6-1T with
+ * SGLang-JAX" page, section 5, activation quantisation): for each row r,
+ *   scale[r] = max_c |a[r][c]| / 448 in fp32 (448 = largest finite e4m3fn
+ *              magnitude; 1 for a row of zeros), and
+ *   q[r][c]  = the e4m3fn code nearest to a[r][c] / scale[r] (fp32 division),
+ *              ties to the even code, magnitudes above 448 saturating to 448,
+ *              the sign bit kept (so -0 and tiny negatives give 0x80).
+ *   a     [rows, lda] bf16 (the first cols columns are read); lda % 8 == 0
+ *   q     [rows, cols] uint8 (written);  scale [rows] fp32 (written)
+ *   cols % 8 == 0 and 0 < cols <= 16384, else MOE_ERR_SHAPE; a 16-byte and q
+ *   8-byte aligned.  Non-finite inputs are outside the contract.
+ */
+moe_status_t moe_quantize_rows(const void* a, int32_t rows, int32_t cols, int64_t lda, uint8_t* q,
+                               float* scale, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status_t status);

@@ -121,3 +121,27 @@ def layer_w8a8(x: np.ndarray, wr: np.ndarray, k: int, expert, shared: Optional[t
         y += expert_ffn_w8a8(xd, w13s, s13s, w2s, s2s, act_shared)
     return dict(y=y, logits=logits, idx=idx, w=w, counts=counts, offsets=offsets,
                 row_token=row_token, row_of_slot=row_of_slot, x_codes=qx, x_scales=sx)
+
+
+def rows_w8a8(tokens, x: np.ndarray, idx: np.ndarray, w: np.ndarray, expert,
+              shared: Optional[tuple] = None, act: str = "silu", act_shared: str = "silu") -> np.ndarray:
+    """W8A8 y for the selected tokens, given the routing (idx, w rows for all
+    tokens).  Every quantisation is per row, so a token's output depends on
+    its own row only and can be evaluated token by token, one expert at a time."""
+    tokens = list(tokens)
+    x = np.asarray(x, np.float64)
+    xd = dequantize_rows(*quantize_rows(x[tokens]))
+    k = idx.shape[1]
+    y = np.zeros((len(tokens), x.shape[1]))
+    by_e = {}
+    for n, t in enumerate(tokens):
+        for j in range(k):
+            by_e.setdefault(int(idx[t, j]), []).append((n, t, j))
+    for e, items in by_e.items():
+        w13, s13, w2, s2 = expert(e)
+        o = expert_ffn_w8a8(xd[[n for n, _, _ in items]], w13, s13, w2, s2, act)
+        for (n, t, j), orow in zip(items, o):
+            y[n] += float(w[t, j]) * orow
+    if shared is not None:
+        y += expert_ffn_w8a8(xd, *shared, act_shared)
+    return y

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 MOE_F32, MOE_BF16, MOE_FP8_E4M3FN = 0, 1, 2
 MOE_ACT_SILU, MOE_ACT_GELU_TANH = 0, 1
 MOE_TILE_AUTO, MOE_TILE_STREAM, MOE_TILE_LDS = 0, 1, 2
+MOE_ACT_QUANT_NONE, MOE_ACT_QUANT_FP8_ROW = 0, 1
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
 
@@ -39,7 +40,7 @@ class MoeError(RuntimeError):
 class MoeProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "D", "E", "k", "I", "I_shared", "act", "act_shared", "renormalize",
-        "act_dtype", "w_dtype", "shared_w_dtype", "tile_policy", "reserved")]
+        "act_dtype", "w_dtype", "shared_w_dtype", "tile_policy", "act_quant")]
 
 
 _vp = ctypes.c_void_p
@@ -70,6 +71,7 @@ _SIG = {
     "moe_stage_count": [],
     "moe_stage_name": [ctypes.c_int32],
     "moe_debug_fp8_to_bf16": [_vp, _vp, ctypes.c_int32, _vp],
+    "moe_quantize_rows": [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _vp, _vp, _vp],
 }
 
 
@@ -121,10 +123,10 @@ def status_string(status: int) -> str:
 
 def make_problem(T, D, E, k, I, I_shared=0, act="silu", act_shared="silu", act_dtype="bf16",
                  w_dtype="bf16", shared_w_dtype=None, tile_policy="auto",
-                 renormalize=True) -> MoeProblem:
+                 renormalize=True, act_quant=MOE_ACT_QUANT_NONE) -> MoeProblem:
     return MoeProblem(T, D, E, k, I, I_shared, ACTS[act], ACTS[act_shared], int(bool(renormalize)),
                       DTYPES[act_dtype], DTYPES[w_dtype],
-                      DTYPES[shared_w_dtype or w_dtype], POLICIES[tile_policy], 0)
+                      DTYPES[shared_w_dtype or w_dtype], POLICIES[tile_policy], int(act_quant))
 
 
 def moe_route(p: MoeProblem, x, w_router, logits, logits_given: bool, topk_idx, topk_w,
@@ -213,6 +215,11 @@ def moe_timing_read():
     cnt = (ctypes.c_int32 * n)()
     _check(lib().moe_timing_read(ms, cnt, n), "moe_timing_read")
     return {moe_stage_name(i): (ms[i], cnt[i]) for i in range(n)}
+
+
+def moe_quantize_rows(a, rows: int, cols: int, lda: int, q, scale, stream=None):
+    _check(lib().moe_quantize_rows(_p(a), rows, cols, lda, _p(q), _p(scale), _stream(stream)),
+           "moe_quantize_rows")
 
 
 def moe_debug_fp8_to_bf16(codes, out, n: int, stream=None):

@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 
-SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn_stream.hip", "ffn_tiled.hip",
+SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn_stream.hip", "ffn_tiled.hip", "actquant.hip",
            "combine.hip"]
 
 ARCH = "gfx950"

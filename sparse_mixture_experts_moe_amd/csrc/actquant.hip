@@ -1,0 +1,114 @@
+// Dynamic per-row fp8 e4m3fn quantisation of bf16 activation rows: the
+// activation quantisation of the "Ling-2.6-1T with SGLang-JAX" page, section
+// 5 (tokens quantised from bf16 to fp8 per token, dynamically, before they go
+// into the matrix unit with the fp8 weights).
+//
+// One block per row: the row's 16-byte chunks stay in registers between the
+// max pass and the conversion pass, so a row is read from HBM once.  The scale
+// is max|a| / 448 (448 being the largest finite e4m3fn magnitude; 1 for a row
+// of zeros), each element becomes the e4m3fn code nearest to a / scale (ties
+// to the even code, saturating at +-448), with both divisions correctly
+// rounded in fp32.
+#include "moe_kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int QT = 256;               // threads per row
+constexpr int QV = 8;                 // 16-byte chunks per thread
+constexpr int QMAX = QT * QV * 8;     // columns a block holds in registers
+
+// e4m3fn code of v with |v| <= 448, from the format: sign, 4 exponent bits
+// (bias 7), 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9.
+// Round to nearest, ties to the even mantissa.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  const float a = fabsf(v);
+  uint32_t code;
+  if (a < 0.015625f) {
+    // below 2^-6 the grid step is 2^-9: rintf rounds a * 2^9 (exact) to
+    // nearest even; 8 is 2^-6, the first normal code
+    code = static_cast<uint32_t>(rintf(a * 512.0f));
+  } else {
+    const uint32_t ab = __float_as_uint(a);
+    uint32_t e = (ab >> 23) - 120u;          // fp32 exponent bias 127 -> 7
+    uint32_t m3 = (ab >> 20) & 7u;
+    const uint32_t rem = ab & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+    if (m3 == 8u) {
+      m3 = 0;
+      ++e;
+    }
+    code = (e << 3) | m3;
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float block_max(float v, float* part) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) part[wave] = v;
+  __syncthreads();
+  float m = part[0];
+#pragma unroll
+  for (int w = 1; w < QT / 64; ++w) m = fmaxf(m, part[w]);
+  return m;
+}
+
+__global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restrict__ a, int cols,
+                                                        int64_t lda, uint8_t* __restrict__ q,
+                                                        float* __restrict__ scale) {
+  __shared__ float part[QT / 64];
+  const int64_t r = blockIdx.x;
+  const uint16_t* row = a + r * lda;
+  const int nch = cols / 8;
+  uint4 v[QV];
+  float amax = 0.f;
+#pragma unroll
+  for (int u = 0; u < QV; ++u) {
+    const int c = threadIdx.x + QT * u;
+    v[u] = c < nch ? *reinterpret_cast<const uint4*>(row + 8 * c) : uint4{0, 0, 0, 0};
+    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(w[j] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
+    }
+  }
+  amax = block_max(amax, part);
+  const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  uint8_t* qrow = q + r * cols;
+#pragma unroll
+  for (int u = 0; u < QV; ++u) {
+    const int c = threadIdx.x + QT * u;
+    if (c >= nch) continue;
+    const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    uint32_t packed[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x0 = __uint_as_float(w[j] << 16), x1 = __uint_as_float(w[j] & 0xFFFF0000u);
+      const float t0 = fminf(fmaxf(__fdiv_rn(x0, s), -448.0f), 448.0f);
+      const float t1 = fminf(fmaxf(__fdiv_rn(x1, s), -448.0f), 448.0f);
+      const uint32_t pair = e4m3_code(t0) | (e4m3_code(t1) << 8);
+      packed[j >> 1] |= pair << (16 * (j & 1));
+    }
+    *reinterpret_cast<uint2*>(qrow + 8 * c) = uint2{packed[0], packed[1]};
+  }
+  if (threadIdx.x == 0) scale[r] = s;
+}
+
+}  // namespace
+
+int quant_max_cols() { return QMAX; }
+
+hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q,
+                             float* scale, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (rows < 0 || cols <= 0 || cols % 8 || cols > QMAX || lda < cols || lda % 8) return hipErrorInvalidValue;
+  if (reinterpret_cast<uintptr_t>(a) % 16 || reinterpret_cast<uintptr_t>(q) % 8) return hipErrorInvalidValue;
+  quant_rows_kernel<<<rows, QT, 0, s>>>(a, cols, lda, q, scale);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -43,7 +43,18 @@ moe_status_t check_problem(const moe_problem_t* p, bool need_ffn, bool need_rout
   if (need_ffn && !combo_ok(p->act_dtype, p->w_dtype)) return MOE_ERR_UNSUPPORTED;
   if (need_ffn && p->I_shared && !combo_ok(p->act_dtype, p->shared_w_dtype))
     return MOE_ERR_UNSUPPORTED;
-  if ((p->renormalize != 0 && p->renormalize != 1) || p->reserved != 0) return MOE_ERR_UNSUPPORTED;
+  if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_UNSUPPORTED;
+  if (p->act_quant != MOE_ACT_QUANT_NONE && p->act_quant != MOE_ACT_QUANT_FP8_ROW) return MOE_ERR_UNSUPPORTED;
+  if (need_ffn && p->act_quant == MOE_ACT_QUANT_FP8_ROW) {
+    // fp8 x fp8 runs on the tiled kernel only, with fp8 weights on both branches
+    if (p->act_dtype != MOE_BF16 || p->w_dtype != MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
+    if (p->I_shared && p->shared_w_dtype != MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
+    if (p->tile_policy == MOE_TILE_STREAM) return MOE_ERR_UNSUPPORTED;
+    const int km = tiled_k_multiple_a8();
+    if (p->D % km || p->I % km || p->I_shared % km) return MOE_ERR_UNSUPPORTED;
+    const int qm = quant_max_cols();
+    if (p->D > qm || p->I > qm || p->I_shared > qm) return MOE_ERR_UNSUPPORTED;
+  }
   return MOE_OK;
 }
 
@@ -87,6 +98,11 @@ bool tiled_fits(const moe_problem_t* p) {
 }
 
 Plan make_plan(const moe_problem_t* p, double mean_rows) {
+  if (p->act_quant == MOE_ACT_QUANT_FP8_ROW) {
+    // fp8 x fp8: the tiled kernel's one-block-per-CU shapes
+    const int shape = mean_rows <= MOE_TALL_MEAN ? TILED_TALL : TILED_WIDE;
+    return Plan{true, 0, tiled_bm(shape), shape};
+  }
   const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16 && tiled_fits(p);
   int policy = p->tile_policy;
   if (policy == MOE_TILE_AUTO) policy = (tiled_ok && mean_rows > 48.0) ? MOE_TILE_LDS : MOE_TILE_STREAM;
@@ -163,14 +179,16 @@ int router_splits(const moe_problem_t* p, const Plan& pl) {
 
 hipError_t run_gemm(const GArgs& g, const Plan& pl, bool gated, int a_dt, int w_dt, int o_dt,
                     hipStream_t s) {
-  if (pl.tiled) return launch_tiled_gemm(g, g.shape, gated, w_dt, o_dt, s);
+  if (pl.tiled) return launch_tiled_gemm(g, g.shape, gated, w_dt, o_dt, a_dt, s);
+  if (a_dt == DT_FP8) return hipErrorInvalidValue;
   return launch_stream_gemm(g, pl.mt, gated, a_dt, w_dt, o_dt, s);
 }
 
 // ---------------------------------------------------------------- timing
-enum Stage { ST_ROUTER = 0, ST_TOPK, ST_PERMUTE, ST_TILES, ST_FFN1, ST_FFN2, ST_COMBINE, ST_COUNT };
+enum Stage { ST_ROUTER = 0, ST_TOPK, ST_PERMUTE, ST_TILES, ST_FFN1, ST_FFN2, ST_COMBINE, ST_QUANT,
+             ST_COUNT };
 const char* kStageNames[ST_COUNT] = {"router_gemm", "topk_softmax", "permute", "tile_table",
-                                     "ffn1_gate_up_act", "ffn2_down", "combine"};
+                                     "ffn1_gate_up_act", "ffn2_down", "combine", "act_quant"};
 
 struct TimingRec {
   int stage;
@@ -237,6 +255,7 @@ struct Carve {
 struct LayerLayout {
   size_t logits, idx, w, counts, offsets, row_token, row_of_slot, blk, rank, tiles, ntiles;
   size_t h, h_sh, o, o_sh, total;
+  size_t xq, sx, hq, sh, hsq, shs;   // fp8 activations and their row scales (act_quant)
   int tile_ub;
   int splits;
   Plan plan;
@@ -265,6 +284,14 @@ LayerLayout layer_layout(const moe_problem_t* p) {
   L.h_sh = c.take(T * p->I_shared * a);
   L.o = c.take(Tk * p->D * a);
   L.o_sh = c.take(p->I_shared ? T * p->D * a : 0);
+  if (p->act_quant == MOE_ACT_QUANT_FP8_ROW) {
+    L.xq = c.take(T * p->D);
+    L.sx = c.take(T * 4);
+    L.hq = c.take(Tk * p->I);
+    L.sh = c.take(Tk * 4);
+    L.hsq = c.take(T * p->I_shared);
+    L.shs = c.take(T * 4);
+  }
   L.total = c.off;
   return L;
 }
@@ -277,6 +304,27 @@ PermLayout perm_layout(const moe_problem_t* p) {
   Carve c;
   L.blk = c.take(static_cast<size_t>(perm_blocks(p->T)) * p->E * 4);
   L.rank = c.take(static_cast<size_t>(p->T) * p->k * 4);
+  L.total = c.off;
+  return L;
+}
+
+// Workspace of moe_grouped_ffn: the M-tile table, and with fp8 activations the
+// quantised A rows (gathered or not: sized for both) and h with their scales.
+struct FfnLayout {
+  size_t tiles, ntiles, aq, sa, hq, sh, total;
+};
+FfnLayout ffn_layout(const moe_problem_t* p, const Plan& pl, int n_groups, int rows_ub) {
+  FfnLayout L{};
+  Carve c;
+  L.tiles = c.take(static_cast<size_t>(routed_tile_ub(rows_ub, n_groups, pl.bm)) * sizeof(GTile));
+  L.ntiles = c.take(16);
+  if (p->act_quant == MOE_ACT_QUANT_FP8_ROW) {
+    const size_t a_rows = static_cast<size_t>(std::max(p->T, rows_ub));
+    L.aq = c.take(a_rows * p->D);
+    L.sa = c.take(a_rows * 4);
+    L.hq = c.take(static_cast<size_t>(rows_ub) * p->I);
+    L.sh = c.take(static_cast<size_t>(rows_ub) * 4);
+  }
   L.total = c.off;
   return L;
 }
@@ -382,10 +430,7 @@ moe_status_t moe_grouped_ffn_workspace_size(const moe_problem_t* p, int32_t n_gr
   if (!bytes) return MOE_ERR_NULL;
   if (n_groups < 1 || n_groups > 1024 || rows_upper_bound < 0) return MOE_ERR_SHAPE;
   const Plan pl = make_plan(p, static_cast<double>(rows_upper_bound) / n_groups);
-  Carve c;
-  c.take(static_cast<size_t>(routed_tile_ub(rows_upper_bound, n_groups, pl.bm)) * sizeof(GTile));
-  c.take(16);
-  *bytes = c.off;
+  *bytes = ffn_layout(p, pl, n_groups, rows_upper_bound).total;
   return MOE_OK;
 }
 
@@ -402,12 +447,24 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t r
   if (rows_upper_bound == 0) return MOE_OK;
   const Plan pl = make_plan(p, static_cast<double>(rows_upper_bound) / n_groups);
   const int tile_ub = routed_tile_ub(rows_upper_bound, n_groups, pl.bm);
+  const FfnLayout FL = ffn_layout(p, pl, n_groups, rows_upper_bound);
   char* w = static_cast<char*>(ws);
-  Carve c;
-  GTile* tiles = reinterpret_cast<GTile*>(w + c.take(static_cast<size_t>(tile_ub) * sizeof(GTile)));
-  int32_t* ntiles = reinterpret_cast<int32_t*>(w + c.take(16));
+  GTile* tiles = reinterpret_cast<GTile*>(w + FL.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(w + FL.ntiles);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool fp8 = p->w_dtype == MOE_FP8_E4M3FN;
+  const bool aq = p->act_quant == MOE_ACT_QUANT_FP8_ROW;
+  const int a_dt = aq ? DT_FP8 : p->act_dtype;
+  const int a_rows = row_token ? p->T : rows_upper_bound;
+  if (row_token && p->T <= 0) return MOE_ERR_SHAPE;
+  uint8_t* aq8 = reinterpret_cast<uint8_t*>(w + FL.aq);
+  float* sa = reinterpret_cast<float*>(w + FL.sa);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(w + FL.hq);
+  float* sh = reinterpret_cast<float*>(w + FL.sh);
+  if (aq) {
+    StageScope sc(ST_QUANT, s);
+    MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(a), a_rows, p->D, p->D, aq8, sa, s));
+  }
   {
     StageScope sc(ST_TILES, s);
     MOE_LAUNCH(launch_build_tiles(offsets, n_groups, pl.bm, rows_upper_bound, tile_ub, pl.tiled,
@@ -418,9 +475,9 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t r
   {
     GSet& S = g1.s[0];
     S.K = p->D;
-    S.a_rows = row_token ? p->T : rows_upper_bound;
-    if (row_token && p->T <= 0) return MOE_ERR_SHAPE;
-    S.a = a;
+    S.a_rows = a_rows;
+    S.a = aq ? static_cast<const void*>(aq8) : a;
+    S.a_scale = aq ? sa : nullptr;
     S.gather = row_token;
     S.lda = p->D;
     S.w = w13;
@@ -442,7 +499,8 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t r
     GSet& S = g2.s[0];
     S.K = p->I;
     S.a_rows = rows_upper_bound;
-    S.a = h;
+    S.a = aq ? static_cast<void*>(hq) : h;
+    S.a_scale = aq ? sh : nullptr;
     S.gather = nullptr;
     S.lda = p->I;
     S.w = w2;
@@ -457,11 +515,15 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t r
   finish_grid(g2, pl, false);
   {
     StageScope sc(ST_FFN1, s);
-    MOE_LAUNCH(run_gemm(g1, pl, true, p->act_dtype, p->w_dtype, p->act_dtype, s));
+    MOE_LAUNCH(run_gemm(g1, pl, true, a_dt, p->w_dtype, p->act_dtype, s));
+  }
+  if (aq) {
+    StageScope sc(ST_QUANT, s);
+    MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(h), rows_upper_bound, p->I, p->I, hq, sh, s));
   }
   {
     StageScope sc(ST_FFN2, s);
-    MOE_LAUNCH(run_gemm(g2, pl, false, p->act_dtype, p->w_dtype, p->act_dtype, s));
+    MOE_LAUNCH(run_gemm(g2, pl, false, a_dt, p->w_dtype, p->act_dtype, s));
   }
   return MOE_OK;
 }
@@ -561,13 +623,27 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
   // 3. grouped FFN: shared branch (dense rows) and routed experts in the same launches
   const bool fp8 = p->w_dtype == MOE_FP8_E4M3FN;
   const bool fp8s = p->shared_w_dtype == MOE_FP8_E4M3FN;
+  // fp8 activations: x quantised per token once, h per row after the gate/up GEMM
+  const bool aq = p->act_quant == MOE_ACT_QUANT_FP8_ROW;
+  const int a_dt = aq ? DT_FP8 : p->act_dtype;
+  uint8_t* xq = reinterpret_cast<uint8_t*>(w + L.xq);
+  float* sx = reinterpret_cast<float*>(w + L.sx);
+  uint8_t* hq = reinterpret_cast<uint8_t*>(w + L.hq);
+  float* sh = reinterpret_cast<float*>(w + L.sh);
+  uint8_t* hsq = reinterpret_cast<uint8_t*>(w + L.hsq);
+  float* shs = reinterpret_cast<float*>(w + L.shs);
+  if (aq) {
+    StageScope sc(ST_QUANT, s);
+    MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(A->x), p->T, p->D, p->D, xq, sx, s));
+  }
   GArgs g1{};
   int si = 0;
   if (p->I_shared) {
     GSet& S = g1.s[si++];
     S.K = p->D;
     S.a_rows = p->T;
-    S.a = A->x;
+    S.a = aq ? static_cast<const void*>(xq) : A->x;
+    S.a_scale = aq ? sx : nullptr;
     S.lda = p->D;
     S.w = A->w13_shared;
     S.scale = fp8s ? A->s13_shared : nullptr;
@@ -583,7 +659,8 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     GSet& S = g1.s[si++];
     S.K = p->D;
     S.a_rows = p->T;
-    S.a = A->x;
+    S.a = aq ? static_cast<const void*>(xq) : A->x;
+    S.a_scale = aq ? sx : nullptr;
     S.gather = row_token;
     S.lda = p->D;
     S.w = A->w13;
@@ -607,7 +684,8 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     GSet& S = g2.s[si++];
     S.K = p->I_shared;
     S.a_rows = p->T;
-    S.a = h_sh;
+    S.a = aq ? static_cast<void*>(hsq) : h_sh;
+    S.a_scale = aq ? shs : nullptr;
     S.lda = p->I_shared;
     S.w = A->w2_shared;
     S.scale = fp8s ? A->s2_shared : nullptr;
@@ -620,7 +698,8 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     GSet& S = g2.s[si++];
     S.K = p->I;
     S.a_rows = static_cast<int32_t>(Tk);
-    S.a = h;
+    S.a = aq ? static_cast<void*>(hq) : h;
+    S.a_scale = aq ? sh : nullptr;
     S.gather = nullptr;
     S.lda = p->I;
     S.w = A->w2;
@@ -655,11 +734,19 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
   } else {
     {
       StageScope sc(ST_FFN1, s);
-      MOE_LAUNCH(run_gemm(g1, pl, true, p->act_dtype, p->w_dtype, p->act_dtype, s));
+      MOE_LAUNCH(run_gemm(g1, pl, true, a_dt, p->w_dtype, p->act_dtype, s));
+    }
+    if (aq) {
+      StageScope sc(ST_QUANT, s);
+      MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(h), static_cast<int>(Tk), p->I, p->I,
+                                   hq, sh, s));
+      if (p->I_shared)
+        MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(h_sh), p->T, p->I_shared,
+                                     p->I_shared, hsq, shs, s));
     }
     {
       StageScope sc(ST_FFN2, s);
-      MOE_LAUNCH(run_gemm(g2, pl, false, p->act_dtype, p->w_dtype, p->act_dtype, s));
+      MOE_LAUNCH(run_gemm(g2, pl, false, a_dt, p->w_dtype, p->act_dtype, s));
     }
   }
   // 4. unpermute + weighted combine + shared branch
@@ -668,6 +755,19 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     MOE_LAUNCH(launch_combine(o, row_of_slot, tw, p->I_shared ? o_sh : nullptr, p->T, p->D, p->k,
                               p->act_dtype, A->y, s));
   }
+  return MOE_OK;
+}
+
+moe_status_t moe_quantize_rows(const void* a, int32_t rows, int32_t cols, int64_t lda, uint8_t* q,
+                               float* scale, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 8 || cols > quant_max_cols() || lda < cols || lda % 8)
+    return MOE_ERR_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!a || !q || !scale) return MOE_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(a) % 16 || reinterpret_cast<uintptr_t>(q) % 8) return MOE_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageScope sc(ST_QUANT, s);
+  MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(a), rows, cols, lda, q, scale, s));
   return MOE_OK;
 }
 

@@ -36,6 +36,13 @@
 // 128-byte activation segments, half the requests per FLOP).  bf16 tiles stay
 // 32 deep, where a deeper stage would leave fewer than three in the LDS ring.
 //
+// With fp8 activations as well (dynamic per-token quantisation, "Ling-2.6-1T
+// with SGLang-JAX" page, section 5: fp8 tokens and fp8 weights straight into
+// the matrix unit, per-token and per-channel scales after the reduction) both
+// tiles hold e4m3fn bytes, the products are 32x32x64 fp8 MFMAs (twice the
+// bf16 rate), stages are 128 deep (128-byte requests for both operands) and
+// the epilogue multiplies by the row's activation scale as well.
+//
 // A tile row of RB bytes holds RB / 16 chunks of 16 bytes; chunk c of row r
 // sits at a position XORed with a few bits of r (upos below), chosen so that
 // the rows sharing a 256-byte line of the 64 banks, and the rows one fragment
@@ -53,22 +60,31 @@ namespace moe {
 namespace {
 
 constexpr int KS = 32;                    // K elements per MFMA sub-step
+#ifndef MOE_TILED_BK8A
+#define MOE_TILED_BK8A 128                // stage depth of fp8 x fp8 tiles (build-time knob)
+#endif
 constexpr int LDS_CU = 160 * 1024;        // LDS per CU
 
-template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8, int BK_> struct Cfg {
+template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8, int BK_, int MF_, bool A8_ = false>
+struct Cfg {
+  static constexpr bool A8 = A8_;                     // fp8 activations (with fp8 weights)
+  static constexpr int MF = MF_;                      // MFMA tile: 16 (16x16x32) or 32 (32x32x16 / x64 fp8)
   static constexpr int BK = BK_;                      // K elements per stage
-  static constexpr int H = BK / KS;                   // sub-steps per stage
+  static constexpr int KSUB = A8 ? 64 : KS;           // K elements per MFMA sub-step
+  static constexpr int H = BK / KSUB;                 // sub-steps per stage
   static constexpr int ROWB = BK * 2;                 // LDS bytes per bf16 tile row
   static constexpr int ROWB8 = BK;                    // LDS bytes per fp8 tile row
+  static constexpr int ROWA = A8 ? ROWB8 : ROWB;      // LDS bytes per activation tile row
   static constexpr int BM = BM_;                      // rows per M-tile
   static constexpr int BNW = BNW_;                    // weight rows per block
   static constexpr int WM = WM_, WN = WN_;            // wavefront grid (rows x weights)
   static constexpr int NW = WM * WN;
   static constexpr int THREADS = 64 * NW;
   static constexpr int BPC = BPC_;                    // blocks per CU
-  static constexpr int TF = BM / WM / 16;             // row fragments per wavefront (4)
-  static constexpr int WF = BNW / WN / 16;            // weight fragments per wavefront (8)
-  static constexpr int A_BYTES = BM * ROWB;
+  static constexpr int TF = BM / WM / MF;             // MF-row fragments per wavefront
+  static constexpr int WF = BNW / WN / MF;            // MF-weight-row fragments per wavefront
+  static constexpr int WPE = NW * BPC / 4;            // wavefronts per SIMD
+  static constexpr int A_BYTES = BM * ROWA;
   static constexpr int B_BYTES = BNW * (FP8 ? ROWB8 : ROWB);
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int S0 = LDS_CU / BPC / STAGE;
@@ -80,8 +96,10 @@ template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8, int BK_> stru
   static constexpr int P1 = (P + H - 1) / H;          // copies issued in a stage's first sub-step
   static_assert(AL * NW * 1024 == A_BYTES && BL * NW * 1024 == B_BYTES, "copy split");
   static_assert(H == 1 || H == 2, "stage depth");
-  static_assert(S >= 3, "ring depth");
-  static_assert(TF == 4 && WF == 8, "wavefront tile is 64 rows x 128 weight rows");
+  static_assert(S >= 3 || (S == 2 && H == 2), "ring depth");
+  static_assert(TF * WF * MF * MF / 64 * WPE <= 256, "accumulators fit the AGPRs");
+  static_assert(WPE == 1 || WPE == 2, "one or two wavefronts per SIMD");
+  static_assert(!A8 || (FP8 && MF == 32), "fp8 activations: fp8 weights, 32x32x64 MFMAs");
 };
 
 // position of 16-byte chunk c in a tile row of RB bytes (an involution in c):
@@ -176,10 +194,12 @@ __device__ __forceinline__ bool remap_block(const GArgs& g, int& logical) {
 #endif
 
 template <class C, bool GATED, int WDT, int ODT>
-__global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g) {
+__global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GArgs g) {
   constexpr bool FP8 = WDT == DT_FP8;
   constexpr int TF = C::TF, WF = C::WF, S = C::S, P = C::P, BNW = C::BNW;
-  constexpr int H = C::H, ROWB = C::ROWB, ROWB8 = C::ROWB8;
+  constexpr int H = C::H, ROWB = C::ROWB, ROWB8 = C::ROWB8, ROWA = C::ROWA, MF = C::MF;
+  constexpr bool A8 = C::A8;
+  constexpr int NKS = (MF == 16 || A8) ? 1 : 2;   // MFMAs per fragment pair and sub-step
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
   // An (empty) statement that names an accumulation register makes the backend
   // select the AGPR form of the MFMAs, so the accumulators live in AGPRs and
@@ -202,9 +222,9 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Wavefront w runs on SIMD w % 4.  The two wavefronts a SIMD hosts get row
-  // groups half a tile apart, so the MFMAs a short tile skips (row fragments
-  // past its last row) come off every SIMD alike.
+  // Wavefront w runs on SIMD w % 4.  With 8 wavefronts, the two a SIMD hosts
+  // get row groups half a tile apart, so the MFMAs a short tile skips (row
+  // fragments past its last row) come off every SIMD alike.
   int wm, wn;
   if constexpr (C::WM == 4) {          // 8 wavefronts: 4 row groups x 2 weight groups
     wm = (wave & 1) + 2 * (wave >> 2);
@@ -213,7 +233,10 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
     wm = wave / C::WN;
     wn = wave % C::WN;
   }
-  const int lr = lane & 15, q = lane >> 4;
+  // 16x16x32: lane (lr, q) holds row / weight row lr of a fragment and K
+  // elements 8q..8q+7 of the sub-step.  32x32x16: lane (l32, hi) holds row
+  // l32 and, in MFMA ks of the sub-step, K chunk 2 hi + ks (8 elements each).
+  const int lr = lane & (MF - 1), q = lane / MF;
   const int K = Sg.K;
   const int split = Sg.ksplit > 1 ? (b - Sg.block0) % Sg.ksplit : 0;
   const int k_len = Sg.ksplit > 1 ? K / Sg.ksplit : K;
@@ -221,8 +244,8 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
   const int nst = k_len / C::BK;
   const int n_out = Sg.n_out;
   const int n0 = nblk * (GATED ? BNW / 2 : BNW);   // first h column (gated) / output column
-  // 16-row fragments of this wavefront that hold tile rows (the rest is padding)
-  const int na = min(TF, max(0, (row1 - row0 - wm * TF * 16 + 15) / 16));
+  // MF-row fragments of this wavefront that hold tile rows (the rest is padding)
+  const int na = min(TF, max(0, (row1 - row0 - wm * TF * MF + MF - 1) / MF));
 
   // ---- HBM -> LDS copy assignments.  Copy instruction j of a stage fills LDS
   // bytes [1024 j, 1024 j + 1024) of the A or B tile; lane l fills the 16 bytes
@@ -230,21 +253,21 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
   // the launcher).  Rows past the tile and weight rows past n_out are fetched
   // from a valid row instead: they only feed accumulator rows / columns the
   // epilogue never stores, so the copy needs no predication.
-  const char* a_base = uniform_ptr(static_cast<const char*>(Sg.a) + static_cast<int64_t>(k_beg) * 2);
+  const char* a_base = uniform_ptr(static_cast<const char*>(Sg.a) + static_cast<int64_t>(k_beg) * (A8 ? 1 : 2));
   uint32_t a_off[C::AL];
 #pragma unroll
   for (int i = 0; i < C::AL; ++i) {
     const int j = wave * C::AL + i;
-    constexpr int LPR = ROWB / 16;                    // lanes per row
+    constexpr int LPR = ROWA / 16;                    // lanes per row
     const int tr = (64 / LPR) * j + lane / LPR;
-    const int c = upos<ROWB>(tr, lane % LPR);        // logical chunk of this position
+    const int c = upos<ROWA>(tr, lane % LPR);        // logical chunk of this position
     const int r = row0 + tr;
     int64_t arow = 0;
     if (r < row1) {
       arow = Sg.gather ? Sg.gather[r] : r;
       if (static_cast<uint64_t>(arow) >= static_cast<uint64_t>(Sg.a_rows)) arow = 0;  // caller error
     }
-    a_off[i] = static_cast<uint32_t>((arow * Sg.lda + c * 8) * 2);
+    a_off[i] = static_cast<uint32_t>(arow * Sg.lda * (A8 ? 1 : 2) + c * 16);
   }
   const char* b_base = uniform_ptr(static_cast<const char*>(Sg.w) +
                                    (group * Sg.w_gstride + k_beg) * (FP8 ? 1 : 2));
@@ -268,7 +291,7 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
   auto issue_one = [&](int st, int k) __attribute__((always_inline)) {
     char* base = smem + (st % S) * C::STAGE;
     if (k < C::AL) {
-      dma16(a_off[k], a_base + st * ROWB, base + (wave * C::AL + k) * 1024);
+      dma16(a_off[k], a_base + st * ROWA, base + (wave * C::AL + k) * 1024);
     } else {
       const int i = k - C::AL;
       dma16(b_off[i], b_base + st * (FP8 ? ROWB8 : ROWB),
@@ -276,80 +299,154 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
     }
   };
 
-  // acc[f][i]: weight fragment f (16 weight rows) x row fragment i (16 rows)
-  f32x4 acc[WF][TF];
+  // acc[f][i]: weight fragment f (MF weight rows) x row fragment i (MF rows)
+  using AccT = typename std::conditional<MF == 16, f32x4, f32x16>::type;
+  AccT acc[WF][TF];
 #pragma unroll
   for (int f = 0; f < WF; ++f)
 #pragma unroll
-    for (int i = 0; i < TF; ++i) acc[f][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < TF; ++i)
+#pragma unroll
+      for (int e = 0; e < MF * MF / 64; ++e) acc[f][i][e] = 0.f;
 
   // weight tile row of fragment f of this wavefront
   auto wrow_of = [&](int f) __attribute__((always_inline)) -> int {
     constexpr int HC = BNW / 2 / C::WN;   // h columns per wavefront (gated)
-    return GATED ? ((f < WF / 2 ? 0 : BNW / 2) + wn * HC + (f % (WF / 2)) * 16 + lr)
-                 : (wn * WF * 16 + f * 16 + lr);
+    return GATED ? ((f < WF / 2 ? 0 : BNW / 2) + wn * HC + (f % (WF / 2)) * MF + lr)
+                 : (wn * WF * MF + f * MF + lr);
   };
+  // a[i][ks]; b[f][ks] (bf16) or b[f][0] (fp8: the lane's weight bytes of the
+  // sub-step, 8 or 16); w[f][ks]: fp8 weights decoded
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-  using BT = typename std::conditional<FP8, u32x2, bf16x8>::type;
-  struct Frag {
-    bf16x8 a[TF];
-    BT b[WF];
-    bf16x8 w[FP8 ? WF : 1];
+  typedef int i32x8 __attribute__((ext_vector_type(8)));
+  using B8 = typename std::conditional<MF == 16, u32x2, u32x4>::type;
+  using BT = typename std::conditional<FP8, B8, bf16x8>::type;
+  struct FragW {     // bf16 activations
+    bf16x8 a[TF][NKS];
+    BT b[WF][FP8 ? 1 : NKS];
+    bf16x8 w[FP8 ? WF : 1][NKS];
   };
-  // fragments of sub-step t (K elements [32 t, 32 t + 32) of the tile): lane
-  // (lr, q) takes K elements 8q..8q+7 of the sub-step
+  struct Frag8 {     // fp8 activations and weights: a lane's 32 bytes of a sub-step
+    i32x8 a[TF];
+    i32x8 b[WF];
+  };
+  using Frag = typename std::conditional<A8, Frag8, FragW>::type;
+  // 16-byte chunk (of the tile row) holding the lane's K elements of sub-step
+  // h of a stage, in MFMA ks
+  auto chunk_of = [&](int h, int ks) __attribute__((always_inline)) -> int {
+    return MF == 16 ? 4 * h + q : 4 * h + 2 * q + ks;
+  };
+  // fragments of sub-step t (K elements [32 t, 32 t + 32) of the tile)
+  // fp8 x fp8 (32x32x64): lane (lr, q) takes bytes [64 h + 32 q, + 32) of its
+  // row in sub-step h, two 16-byte chunks, for either operand
   auto readf = [&](Frag& F, int t) __attribute__((always_inline)) {
     const int h = t % H;
     const char* base = smem + ((t / H) % S) * C::STAGE;
     const char* bb = base + C::A_BYTES;
+    if constexpr (A8) {
+      auto rd = [&](const char* tile, int row) __attribute__((always_inline)) -> i32x8 {
+        const int c0 = 4 * h + 2 * q;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + row * ROWB8 + upos<ROWB8>(row, c0) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + row * ROWB8 + upos<ROWB8>(row, c0 + 1) * 16);
+        return i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                     static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                     static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+      };
+#pragma unroll
+      for (int i = 0; i < TF; ++i) F.a[i] = rd(base, wm * TF * MF + MF * i + lr);
+#pragma unroll
+      for (int f = 0; f < WF; ++f) F.b[f] = rd(bb, wrow_of(f));
+      return;
+    } else {
 #pragma unroll
     for (int i = 0; i < TF; ++i) {
-      const int r = wm * TF * 16 + 16 * i + lr;
-      F.a[i] = *reinterpret_cast<const bf16x8*>(base + r * ROWB + upos<ROWB>(r, 4 * h + q) * 16);
+      const int r = wm * TF * MF + MF * i + lr;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        F.a[i][ks] = *reinterpret_cast<const bf16x8*>(base + r * ROWB + upos<ROWB>(r, chunk_of(h, ks)) * 16);
     }
 #pragma unroll
     for (int f = 0; f < WF; ++f) {
       const int tr = wrow_of(f);
-      if constexpr (FP8)
-        F.b[f] = *reinterpret_cast<const u32x2*>(bb + tr * ROWB8 + upos<ROWB8>(tr, 2 * h + (q >> 1)) * 16 +
-                                                 (q & 1) * 8);
-      else
-        F.b[f] = *reinterpret_cast<const bf16x8*>(bb + tr * ROWB + upos<ROWB>(tr, 4 * h + q) * 16);
+      if constexpr (FP8) {
+        if constexpr (MF == 16)
+          F.b[f][0] = *reinterpret_cast<const B8*>(bb + tr * ROWB8 + upos<ROWB8>(tr, 2 * h + (q >> 1)) * 16 +
+                                                   (q & 1) * 8);
+        else
+          F.b[f][0] = *reinterpret_cast<const B8*>(bb + tr * ROWB8 + upos<ROWB8>(tr, 2 * h + q) * 16);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          F.b[f][ks] = *reinterpret_cast<const bf16x8*>(bb + tr * ROWB + upos<ROWB>(tr, chunk_of(h, ks)) * 16);
+      }
+    }
     }
   };
   // Use the fragments in an empty statement so that the compiler's own wait
   // for them lands here (before the barrier) and not in front of the MFMAs.
   auto settle = [&](Frag& F) __attribute__((always_inline)) {
+    if constexpr (A8) {
+      // (a 32-byte "v" operand is not valid for the host target: device pass only)
+#if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
-    for (int i = 0; i < TF; ++i) asm volatile("" ::"v"(F.a[i]));
+      for (int i = 0; i < TF; ++i) asm volatile("" ::"v"(F.a[i]));
 #pragma unroll
-    for (int f = 0; f < WF; ++f) asm volatile("" ::"v"(F.b[f]));
+      for (int f = 0; f < WF; ++f) asm volatile("" ::"v"(F.b[f]));
+#endif
+      return;
+    } else {
+#pragma unroll
+    for (int i = 0; i < TF; ++i)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) asm volatile("" ::"v"(F.a[i][ks]));
+#pragma unroll
+    for (int f = 0; f < WF; ++f)
+#pragma unroll
+      for (int ks = 0; ks < (FP8 ? 1 : NKS); ++ks) asm volatile("" ::"v"(F.b[f][ks]));
     if constexpr (FP8) {
 #pragma unroll
-      for (int f = 0; f < WF; ++f) F.w[f] = fp8x8_to_bf16x8(F.b[f][0], F.b[f][1]);
+      for (int f = 0; f < WF; ++f) {
+        F.w[f][0] = fp8x8_to_bf16x8(F.b[f][0][0], F.b[f][0][1]);
+        if constexpr (MF == 32) F.w[f][1] = fp8x8_to_bf16x8(F.b[f][0][2], F.b[f][0][3]);
+      }
+    }
     }
   };
   // MFMAs of one sub-step, row fragment by row fragment; fragments past the
   // tile's last row (i >= na, a uniform branch) are skipped.  When dst >= 0,
-  // copies K0..K1-1 of stage dst are spread between the row-fragment groups so
-  // their issue overlaps the MFMAs.
+  // copies K0..K1-1 of stage dst are spread between the MFMA groups so their
+  // issue overlaps the MFMAs.
   auto mma = [&](const Frag& F, int dst, auto k0, auto k1) __attribute__((always_inline)) {
     constexpr int K0 = decltype(k0)::value, NK = decltype(k1)::value - K0;
-    constexpr int PER = (NK + TF - 1) / TF;
+    constexpr int G = TF * NKS;
+    constexpr int PER = (NK + G - 1) / G;
 #pragma unroll
     for (int i = 0; i < TF; ++i) {
-      if (i < na) {
 #pragma unroll
-        for (int f = 0; f < WF; ++f) {
-          bf16x8 w;
-          if constexpr (FP8) w = F.w[f];
-          else w = F.b[f];
-          acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, F.a[i], acc[f][i], 0, 0, 0);
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (i < na) {
+#pragma unroll
+          for (int f = 0; f < WF; ++f) {
+            if constexpr (A8) {
+              // e4m3 x e4m3 (format codes 0), unit block scales (exponent 127)
+              acc[f][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[f], F.a[i], acc[f][i], 0, 0,
+                                                                          0, 127, 0, 127);
+            } else {
+              bf16x8 w;
+              if constexpr (FP8) w = F.w[f][ks];
+              else w = F.b[f][ks];
+              if constexpr (MF == 16)
+                acc[f][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w, F.a[i][ks], acc[f][i], 0, 0, 0);
+              else
+                acc[f][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w, F.a[i][ks], acc[f][i], 0, 0, 0);
+            }
+          }
         }
-      }
+        const int gi = i * NKS + ks;
 #pragma unroll
-      for (int u = 0; u < PER; ++u)
-        if (i * PER + u < NK && dst >= 0) issue_one(dst, K0 + i * PER + u);
+        for (int u = 0; u < PER; ++u)
+          if (gi * PER + u < NK && dst >= 0) issue_one(dst, K0 + gi * PER + u);
+      }
     }
   };
   using I0 = std::integral_constant<int, 0>;
@@ -397,18 +494,21 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
   }
   wait_vm<0>();   // no copy may still be in flight when the block retires
 
-  // ---- epilogue: lane holds C[row lr of fragment i][cols 4q..4q+3 of fragment f];
-  // the 4 columns are stored together (8 bytes in bf16, 16 in fp32).  Column
-  // groups outermost, so each group's scales are loaded once and the
-  // accumulators are consumed in order.
+  // ---- epilogue.  16x16: lane (lr, q) holds C[row lr of fragment i][columns
+  // 4q..4q+3 of fragment f].  32x32: accumulator element 4g + j of lane
+  // (lr, q) holds C[row lr][column 8g + 4q + j].  Each group of 4 columns is
+  // stored together (8 bytes in bf16, 16 in fp32); column groups outermost, so
+  // each group's scales are loaded once.
   const float* sc = Sg.scale ? Sg.scale + group * Sg.s_gstride : nullptr;
   constexpr int OCOLS = GATED ? BNW / 2 / C::WN : BNW / C::WN;   // output columns per wavefront
+  constexpr int NG = MF / 8;                                     // column groups per fragment and lane
   const int col_w = n0 + wn * OCOLS;
   char* outb = static_cast<char*>(Sg.out) + split * Sg.split_stride * (ODT == DT_F32 ? 4 : 2);
 #pragma unroll
-  for (int f = 0; f < (GATED ? WF / 2 : WF); ++f) {
-    const int col = col_w + f * 16 + 4 * q;   // first of the lane's 4 columns
-    const bool col_ok = col < n_out;          // n_out is a multiple of 4
+  for (int fg = 0; fg < (GATED ? WF / 2 : WF) * NG; ++fg) {
+    const int f = fg / NG, g = fg % NG;
+    const int col = col_w + f * MF + (MF == 16 ? 4 * q : 8 * g + 4 * q);   // first of the lane's 4 columns
+    const bool col_ok = col < n_out;                                       // n_out is a multiple of 4
     float s0[4], s1[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -417,15 +517,18 @@ __global__ __launch_bounds__(C::THREADS, 2) void tiled_gemm_kernel(const GArgs g
     }
 #pragma unroll
     for (int i = 0; i < TF; ++i) {
-      const int r = row0 + wm * TF * 16 + i * 16 + lr;
+      const int r = row0 + wm * TF * MF + i * MF + lr;
       if (r >= row1 || !col_ok) continue;
+      float ra = 1.f;   // the row's activation scale (fp8 activations)
+      if constexpr (A8) ra = Sg.a_scale[Sg.gather ? Sg.gather[r] : r];
       float v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const int e = 4 * g + j;
         if constexpr (GATED)
-          v[j] = act_fn(Sg.act, acc[f][i][j] * s0[j]) * (acc[f + WF / 2][i][j] * s1[j]);
+          v[j] = act_fn(Sg.act, acc[f][i][e] * ra * s0[j]) * (acc[f + WF / 2][i][e] * ra * s1[j]);
         else
-          v[j] = acc[f][i][j] * s0[j];
+          v[j] = acc[f][i][e] * ra * s0[j];
       }
       const int64_t o = static_cast<int64_t>(r) * Sg.ldo + col;
       if constexpr (ODT == DT_BF16) {
@@ -446,11 +549,20 @@ hipError_t launch_one(const GArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BNW, int WM, int WN, int BPC>
-hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, hipStream_t s) {
-  using CB = Cfg<BM, BNW, WM, WN, BPC, false, 32>;
+template <int BM, int BNW, int WM, int WN, int BPC, int MF>
+hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, int a_dtype, hipStream_t s) {
+  using CB = Cfg<BM, BNW, WM, WN, BPC, false, 32, MF>;
   // fp8 weights 64 deep where three such stages fit in the block's LDS share
-  using C8 = Cfg<BM, BNW, WM, WN, BPC, true, (BPC == 1 ? 64 : 32)>;
+  using C8 = Cfg<BM, BNW, WM, WN, BPC, true, (BPC == 1 ? 64 : 32), MF>;
+  if (a_dtype == DT_FP8) {
+    // fp8 x fp8: one block per CU, 32x32x64 MFMAs
+    if constexpr (BPC == 1) {
+      using CA = Cfg<BM, BNW, WM, WN, 1, true, MOE_TILED_BK8A, 32, true>;
+      if (w_dtype != DT_FP8 || out_dtype != DT_BF16) return hipErrorInvalidValue;
+      return gated ? launch_one<CA, true, DT_FP8, DT_BF16>(g, s) : launch_one<CA, false, DT_FP8, DT_BF16>(g, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (gated) {
     if (w_dtype == DT_BF16 && out_dtype == DT_BF16) return launch_one<CB, true, DT_BF16, DT_BF16>(g, s);
     if (w_dtype == DT_FP8 && out_dtype == DT_BF16) return launch_one<C8, true, DT_FP8, DT_BF16>(g, s);
@@ -471,6 +583,9 @@ int tiled_bm(int shape) { return shape == TILED_TALL ? 256 : 128; }
 
 int tiled_k_multiple() { return 2 * KS; }
 
+// fp8 x fp8: K a multiple of the 128-deep stage (or of two 64-deep ones)
+int tiled_k_multiple_a8() { return 128; }
+
 int tiled_blocks_n(int shape, bool gated, int n_out) {
   const int w = gated ? block_width(shape) / 2 : block_width(shape);
   return (n_out + w - 1) / w;
@@ -482,18 +597,19 @@ bool tiled_offsets_fit(int64_t a_rows, int64_t lda, int64_t w_rows, int64_t K, i
 }
 
 hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype, int out_dtype,
-                             hipStream_t s) {
+                             int a_dtype, hipStream_t s) {
   if (g.total_blocks <= 0) return hipSuccess;
   for (int i = 0; i < g.nsets; ++i) {
     const GSet& S = g.s[i];
     const int ks = S.ksplit > 1 ? S.ksplit : 1;
     if ((S.K / ks) % (2 * KS) || S.bm != tiled_bm(shape) || S.n_out % 4) return hipErrorInvalidValue;
+    if (a_dtype == DT_FP8 && ((S.K / ks) % tiled_k_multiple_a8() || !S.a_scale)) return hipErrorInvalidValue;
     if (!tiled_offsets_fit(S.a_rows, S.lda, S.NB, S.K, w_dtype)) return hipErrorInvalidValue;
   }
   switch (shape) {
-    case TILED_TALL: return dispatch<256, 256, 4, 2, 1>(g, gated, w_dtype, out_dtype, s);
-    case TILED_WIDE: return dispatch<128, 512, 2, 4, 1>(g, gated, w_dtype, out_dtype, s);
-    case TILED_NARROW: return dispatch<128, 256, 2, 2, 2>(g, gated, w_dtype, out_dtype, s);
+    case TILED_TALL: return dispatch<256, 256, 4, 2, 1, 16>(g, gated, w_dtype, out_dtype, a_dtype, s);
+    case TILED_WIDE: return dispatch<128, 512, 2, 4, 1, 16>(g, gated, w_dtype, out_dtype, a_dtype, s);
+    case TILED_NARROW: return dispatch<128, 256, 2, 2, 2, 16>(g, gated, w_dtype, out_dtype, a_dtype, s);
   }
   return hipErrorInvalidValue;
 }

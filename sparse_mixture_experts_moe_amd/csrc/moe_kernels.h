@@ -12,6 +12,7 @@ enum : int { ACT_SILU = 0, ACT_GELU_TANH = 1 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));   // 16 raw bytes in registers
 
 // bf16 storage is handled as raw uint16_t.
@@ -40,6 +41,7 @@ struct GSet {
   const void* a;            // A storage, row stride lda elements
   const int32_t* gather;    // A row of set row r = gather ? gather[r] : r
   int64_t lda;
+  const float* a_scale;     // fp8 A: per-A-row (storage row) dequantisation scale
   const void* w;            // [groups][NB][K] weight storage
   const float* scale;       // [groups][NB] per-output-channel scales or null
   int64_t w_gstride;        // elements between groups (NB*K)
@@ -173,13 +175,23 @@ int stream_max_mt(int a_dtype);              // largest mt the stream kernel run
 // 128 x 512 and TILED_NARROW 128 x 256 (two blocks per CU).  Every set's bm
 // must be tiled_bm(shape).
 enum : int { TILED_TALL = 0, TILED_WIDE = 1, TILED_NARROW = 2 };
+// a_dtype DT_FP8 (fp8 activations with fp8 weights, bf16 output, one block
+// per CU shapes only) needs every set's a_scale.
 hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype, int out_dtype,
-                             hipStream_t s);
+                             int a_dtype, hipStream_t s);
 int tiled_bm(int shape);
 int tiled_k_multiple();                      // every K (slice) must be a multiple of this
+int tiled_k_multiple_a8();                   // the same with fp8 activations
 int tiled_blocks_n(int shape, bool gated, int n_out);
 // The tiled GEMM addresses A rows and one group's weights with 32-bit byte offsets.
 bool tiled_offsets_fit(int64_t a_rows, int64_t lda, int64_t w_rows, int64_t K, int w_dtype);
+
+// Dynamic per-row fp8 quantisation of bf16 rows: scale[r] = max|a[r]| / 448
+// (1 for a zero row), q[r][c] = e4m3fn(a[r][c] / scale[r]) rounded to nearest
+// even, saturating.  cols % 8 == 0, cols <= quant_max_cols(); q is [rows][cols].
+int quant_max_cols();
+hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q,
+                             float* scale, hipStream_t s);
 
 // Decode n (multiple of 8) fp8 e4m3fn codes to bf16 with the GEMM's own decoder.
 hipError_t launch_fp8_decode(const uint8_t* codes, uint16_t* out, int n, hipStream_t s);

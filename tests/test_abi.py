@@ -65,13 +65,50 @@ def _ok_problem(**over):
     (dict(tile_policy=5), B.MOE_ERR_DTYPE),
     (dict(w_dtype=B.MOE_BF16), B.MOE_ERR_UNSUPPORTED),              # f32 act x bf16 weights
     (dict(act_dtype=B.MOE_FP8_E4M3FN), B.MOE_ERR_UNSUPPORTED),
-    (dict(renormalize=2), B.MOE_ERR_UNSUPPORTED), (dict(reserved=1), B.MOE_ERR_UNSUPPORTED),
+    (dict(renormalize=2), B.MOE_ERR_UNSUPPORTED), (dict(act_quant=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(act_quant=1), B.MOE_ERR_UNSUPPORTED),                       # fp32 layer: no fp8 path
     (dict(renormalize=0), B.MOE_OK),
 ])
 def test_validation_codes(lib, over, status):
     p = _ok_problem(**over)
     n = ctypes.c_size_t(0)
     assert lib.moe_layer_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+
+
+def _fp8_problem(**over):
+    p = B.make_problem(64, 256, 8, 2, 128, 128, act_dtype="bf16", w_dtype="fp8",
+                       act_quant=B.MOE_ACT_QUANT_FP8_ROW)
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(), B.MOE_OK),
+    (dict(w_dtype=B.MOE_BF16, shared_w_dtype=B.MOE_BF16), B.MOE_ERR_UNSUPPORTED),  # needs fp8 weights
+    (dict(shared_w_dtype=B.MOE_BF16), B.MOE_ERR_UNSUPPORTED),
+    (dict(tile_policy=B.MOE_TILE_STREAM), B.MOE_ERR_UNSUPPORTED),
+    (dict(D=192), B.MOE_ERR_UNSUPPORTED), (dict(I=64), B.MOE_ERR_UNSUPPORTED),   # K multiple of 128
+    (dict(I_shared=0), B.MOE_OK), (dict(D=32768), B.MOE_ERR_UNSUPPORTED),
+])
+def test_act_quant_validation(lib, over, status):
+    p = _fp8_problem(**over)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_layer_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+    if status == B.MOE_OK:
+        p0 = _fp8_problem(act_quant=0, **over)
+        assert n.value > B.moe_layer_workspace_size(p0)    # fp8 copies of x and h live there
+
+
+def test_quantize_rows_validation(lib):
+    fake = 4096
+    assert lib.moe_quantize_rows(fake, 4, 12, 16, fake, fake, None) == B.MOE_ERR_SHAPE   # cols % 8
+    assert lib.moe_quantize_rows(fake, 4, 16, 8, fake, fake, None) == B.MOE_ERR_SHAPE    # lda < cols
+    assert lib.moe_quantize_rows(fake, 4, 16, 20, fake, fake, None) == B.MOE_ERR_SHAPE   # lda % 8
+    assert lib.moe_quantize_rows(fake, 4, 1 << 15, 1 << 15, fake, fake, None) == B.MOE_ERR_SHAPE
+    assert lib.moe_quantize_rows(fake, -1, 16, 16, fake, fake, None) == B.MOE_ERR_SHAPE
+    assert lib.moe_quantize_rows(None, 4, 16, 16, fake, fake, None) == B.MOE_ERR_NULL
+    assert lib.moe_quantize_rows(None, 0, 16, 16, None, None, None) == B.MOE_OK
 
 
 def test_null_and_workspace_errors(lib):

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from oracle.actquant import (E4M3_MAX, dequantize_rows, encode_e4m3fn, layer_w8a8,
-                             quantize_rows, round_bf16)
+                             quantize_rows, round_bf16, rows_w8a8)
 from oracle.formats import fp8_e4m3fn_table
 from oracle.moe import layer, rel_err
 from test_oracle_layer import decoded
@@ -122,3 +122,12 @@ def test_w8a8_layer_is_close_to_the_plain_definition(name):
         assert np.array_equal(np.asarray(q[n]), np.asarray(ref[n]))
     err = rel_err(q["y"], ref["y"])
     assert 1e-4 < err < 0.08, err
+
+
+def test_token_by_token_evaluation_matches_the_whole_layer():
+    cfg = W8A8["ling_prefill_like"]
+    x, wr, experts, shared = decoded(generate(cfg, seed=7))
+    q = layer_w8a8(x, wr, cfg.k, experts, shared, cfg.act, cfg.act_shared)
+    toks = [0, 5, 17, 39]
+    y = rows_w8a8(toks, x, q["idx"], q["w"], experts, shared, cfg.act, cfg.act_shared)
+    assert np.allclose(y, q["y"][toks], rtol=1e-12, atol=1e-12)
