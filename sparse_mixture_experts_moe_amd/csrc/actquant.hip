@@ -3,8 +3,8 @@
 // 5 (tokens quantised from bf16 to fp8 per token, dynamically, before they go
 // into the matrix unit with the fp8 weights).
 //
-// One block per row: the row's 16-byte chunks stay in registers between the
-// max pass and the conversion pass, so a row is read from HBM once.  The scale
+// A row's 16-byte chunks stay in registers between the max pass and the
+// conversion pass, so a row is read from HBM once.  The scale
 // is max|a| / 448 (448 being the largest finite e4m3fn magnitude; 1 for a row
 // of zeros), each element becomes the e4m3fn code nearest to a / scale (ties
 // to the even code, saturating at +-448), with both divisions correctly
@@ -14,9 +14,7 @@
 namespace moe {
 namespace {
 
-constexpr int QT = 256;               // threads per row
-constexpr int QV = 8;                 // 16-byte chunks per thread
-constexpr int QMAX = QT * QV * 8;     // columns a block holds in registers
+constexpr int QMAX = 16384;           // widest row: 64 lanes x 32 chunks of 8
 
 // e4m3fn code of v with |v| <= 448, from the format: sign, 4 exponent bits
 // (bias 7), 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9.
@@ -44,31 +42,27 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return sign | code;
 }
 
-__device__ __forceinline__ float block_max(float v, float* part) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) part[wave] = v;
-  __syncthreads();
-  float m = part[0];
-#pragma unroll
-  for (int w = 1; w < QT / 64; ++w) m = fmaxf(m, part[w]);
-  return m;
-}
-
-__global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restrict__ a, int cols,
-                                                        int64_t lda, uint8_t* __restrict__ q,
-                                                        float* __restrict__ scale) {
-  __shared__ float part[QT / 64];
-  const int64_t r = blockIdx.x;
+// One wavefront per row, 4 rows per block: lane l holds the row's 16-byte
+// chunks l, l + 64, ... (NCH of them) in registers between the max and the
+// conversion, so a row is read once and the reduction is a wavefront butterfly.
+template <int NCH>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ a, int rows,
+                                                         int cols, int64_t lda, uint8_t* __restrict__ q,
+                                                         float* __restrict__ scale) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
   const uint16_t* row = a + r * lda;
   const int nch = cols / 8;
-  uint4 v[QV];
+  uint4 v[NCH];
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int c = lane + 64 * u;
+    v[u] = c < nch ? *reinterpret_cast<const uint4*>(row + 8 * c) : uint4{0, 0, 0, 0};
+  }
   float amax = 0.f;
 #pragma unroll
-  for (int u = 0; u < QV; ++u) {
-    const int c = threadIdx.x + QT * u;
-    v[u] = c < nch ? *reinterpret_cast<const uint4*>(row + 8 * c) : uint4{0, 0, 0, 0};
+  for (int u = 0; u < NCH; ++u) {
     const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -76,12 +70,13 @@ __global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restri
       amax = fmaxf(amax, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
     }
   }
-  amax = block_max(amax, part);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
   const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
   uint8_t* qrow = q + r * cols;
 #pragma unroll
-  for (int u = 0; u < QV; ++u) {
-    const int c = threadIdx.x + QT * u;
+  for (int u = 0; u < NCH; ++u) {
+    const int c = lane + 64 * u;
     if (c >= nch) continue;
     const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
     uint32_t packed[2] = {0, 0};
@@ -95,7 +90,14 @@ __global__ __launch_bounds__(QT) void quant_rows_kernel(const uint16_t* __restri
     }
     *reinterpret_cast<uint2*>(qrow + 8 * c) = uint2{packed[0], packed[1]};
   }
-  if (threadIdx.x == 0) scale[r] = s;
+  if (lane == 0) scale[r] = s;
+}
+
+template <int NCH>
+hipError_t go(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q, float* scale,
+              hipStream_t s) {
+  quant_rows_kernel<NCH><<<(rows + 3) / 4, 256, 0, s>>>(a, rows, cols, lda, q, scale);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -107,8 +109,13 @@ hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, int64_t lda,
   if (rows == 0) return hipSuccess;
   if (rows < 0 || cols <= 0 || cols % 8 || cols > QMAX || lda < cols || lda % 8) return hipErrorInvalidValue;
   if (reinterpret_cast<uintptr_t>(a) % 16 || reinterpret_cast<uintptr_t>(q) % 8) return hipErrorInvalidValue;
-  quant_rows_kernel<<<rows, QT, 0, s>>>(a, cols, lda, q, scale);
-  return hipGetLastError();
+  const int nch = (cols / 8 + 63) / 64;   // chunks per lane
+  if (nch <= 1) return go<1>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 2) return go<2>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 4) return go<4>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 8) return go<8>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 16) return go<16>(a, rows, cols, lda, q, scale, s);
+  return go<32>(a, rows, cols, lda, q, scale, s);
 }
 
 }  // namespace moe
