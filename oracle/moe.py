@@ -132,15 +132,22 @@ def expert_ffn(X: np.ndarray, w13: np.ndarray, s13: Optional[np.ndarray],
 
 
 def experts_from_bits(w13_bits, s13, w2_bits, s2, dtype: str) -> ExpertFn:
-    """Accessor e -> decoded (w13, s13, w2, s2) over raw [E,...] storage."""
+    """Accessor e -> decoded (w13, s13, w2, s2) over raw [E,...] storage (for
+    MXFP4 the block scales are folded into the decoded weights and s = None)."""
+    from .mx import decode_weight
+
     def get(e):
-        return (decode(w13_bits[e], dtype), None if s13 is None else s13[e],
-                decode(w2_bits[e], dtype), None if s2 is None else s2[e])
+        w13, a = decode_weight(w13_bits[e], None if s13 is None else s13[e], dtype)
+        w2, b = decode_weight(w2_bits[e], None if s2 is None else s2[e], dtype)
+        return w13, a, w2, b
     return get
 
 
 def shared_from_bits(w13_bits, s13, w2_bits, s2, dtype: str):
-    return (decode(w13_bits, dtype), s13, decode(w2_bits, dtype), s2)
+    from .mx import decode_weight
+    w13, a = decode_weight(w13_bits, s13, dtype)
+    w2, b = decode_weight(w2_bits, s2, dtype)
+    return w13, a, w2, b
 
 
 # ---------------------------------------------------------------- whole layer

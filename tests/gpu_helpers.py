@@ -9,6 +9,7 @@ import numpy as np
 import torch
 
 from oracle.formats import decode
+from oracle.mx import decode_weight
 from oracle.moe import (expert_ffn, experts_from_bits, layer, permute, rel_err,
                         shared_from_bits, topk_softmax)
 from sparse_mixture_experts_moe_amd import binding as B
@@ -62,11 +63,15 @@ def oracle_inputs(wl):
 
     def expert(e):
         w13, s13, w2, s2 = host_expert(wl, e)
-        return decode(w13, c.w_dtype), s13, decode(w2, c.w_dtype), s2
+        a, sa = decode_weight(w13, s13, c.w_dtype)
+        b, sb = decode_weight(w2, s2, c.w_dtype)
+        return a, sa, b, sb
     sh = host_shared(wl)
     shared = None
     if sh is not None:
-        shared = (decode(sh[0], c.shared_w_dtype), sh[1], decode(sh[2], c.shared_w_dtype), sh[3])
+        a, sa = decode_weight(sh[0], sh[1], c.shared_w_dtype)
+        b, sb = decode_weight(sh[2], sh[3], c.shared_w_dtype)
+        shared = (a, sa, b, sb)
     return x, wr, expert, shared
 
 

@@ -22,7 +22,14 @@ Recipe (both sides read the same tensors):
     expert by expert: W13[e] ~ N(0,1/D) [2I,D], then W2[e] ~ N(0,1/I) [D,I];
     then the shared/dense branch W13s [2Is,D], W2s [D,Is];
   * casts: bf16 by round-to-nearest-even; fp8 e4m3fn per output row with
-    s[n] = amax_n/448 and q = RNE(clamp(W[n,:]/s[n], -448, 448)).
+    s[n] = amax_n/448 and q = RNE(clamp(W[n,:]/s[n], -448, 448)); MXFP4 (the
+    W4A8 weights of the CANN Qwen3-MoE page, in the Open Compute Project
+    microscaling format): per block of 32 consecutive K elements the E8M0 scale
+    exponent is floor(log2 amax) - 2, the e2m1 codes are the nearest values of
+    W / 2**exp (ties to the even code, saturating at 6).  MXFP4 storage: two
+    codes per byte (element 2j in the low nibble), [.., N, K/2]; scales grouped
+    by 128 K elements, [.., K/128, N, 4] (a row's four block scales of a group
+    side by side).
 Rows [0,I) of W13 are the gate projection, rows [I,2I) the up projection.
 """
 from __future__ import annotations
@@ -52,7 +59,7 @@ class MoEConfig:
     act: str        # "silu" (SwiGLU) or "gelu_tanh" (GEGLU)
     act_shared: str
     act_dtype: str  # "f32" | "bf16"  (x, router weight, y)
-    w_dtype: str    # "f32" | "bf16" | "fp8"  (routed W13 / W2)
+    w_dtype: str    # "f32" | "bf16" | "fp8" | "mxfp4"  (routed W13 / W2)
     shared_w_dtype: str
     zipf: bool = False
 
@@ -74,6 +81,12 @@ CONFIGS = {
     "gemma": _cfg("gemma", 2048, 2816, 128, 8, 704, 2112, "gelu_tanh", "bf16", "bf16"),
     "ling_prefill": _cfg("ling_prefill", 16384, 8192, 256, 8, 2048, 2048, "silu", "bf16", "fp8"),
     "ling_decode": _cfg("ling_decode", 512, 8192, 256, 8, 2048, 2048, "silu", "bf16", "fp8"),
+    # the Ling layer with MXFP4 expert weights (the W4A8 setting of the CANN
+    # Qwen3-MoE page); not one of the five configurations the pages measure
+    "ling_prefill_mxfp4": _cfg("ling_prefill_mxfp4", 16384, 8192, 256, 8, 2048, 2048, "silu", "bf16",
+                               "mxfp4"),
+    "ling_decode_mxfp4": _cfg("ling_decode_mxfp4", 512, 8192, 256, 8, 2048, 2048, "silu", "bf16",
+                              "mxfp4"),
 }
 
 
@@ -114,9 +127,36 @@ def _quant_fp8_rows(w: torch.Tensor):
     return q, s.to(torch.float32)
 
 
+_E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _quant_mxfp4(w: torch.Tensor):
+    """MXFP4 quantisation of an fp32 matrix [N, K] (K a multiple of 128):
+    (packed codes uint8 [N, K/2], scales uint8 [K/128, N, 4])."""
+    N, K = w.shape
+    blocks = w.reshape(N, K // 32, 32)
+    amax = blocks.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)                            # amax = m * 2**ex, m in [0.5, 1)
+    shared = torch.where(amax > 0, ex - 1, torch.full_like(ex, -127)) - 2
+    shared = shared.clamp(-127, 127)
+    scaled = blocks / torch.exp2(shared.to(torch.float32)).unsqueeze(-1)
+    mag = scaled.abs().clamp(max=6.0)
+    vals = torch.tensor(_E2M1_MAG, device=w.device)
+    mids = (vals[1:] + vals[:-1]) / 2
+    idx = torch.bucketize(mag, mids, right=True)         # a tie goes to the upper code here
+    tie = (idx > 0) & (mag == mids[(idx - 1).clamp(min=0)])
+    idx = torch.where(tie & (idx % 2 == 1), idx - 1, idx)   # ... and back to the even one
+    codes = (idx | torch.where(torch.signbit(scaled), 8, 0)).to(torch.uint8).reshape(N, K)
+    packed = codes[:, 0::2] | (codes[:, 1::2] << 4)
+    scales = (shared + 127).to(torch.uint8).reshape(N, K // 128, 4).permute(1, 0, 2).contiguous()
+    return packed, scales
+
+
 def _cast(w: torch.Tensor, dtype: str):
     if dtype == "fp8":
         return _quant_fp8_rows(w)
+    if dtype == "mxfp4":
+        return _quant_mxfp4(w)
     return w.to(_TORCH_DT[dtype]), None
 
 
@@ -141,22 +181,28 @@ def generate(cfg: MoEConfig, seed: int = 0, weight_device: str = "cpu",
     x, wr = router_inputs(cfg, seed, zipf_alpha)
     dev = torch.device(weight_device)
     gw = torch.Generator(device=dev).manual_seed(seed + 2)
-    wdt = {"fp8": torch.float8_e4m3fn}.get(cfg.w_dtype, _TORCH_DT.get(cfg.w_dtype))
-    w13 = torch.empty((E, 2 * I, D), dtype=wdt, device=dev)
-    w2 = torch.empty((E, D, I), dtype=wdt, device=dev)
+    mx = cfg.w_dtype == "mxfp4"
+    wdt = {"fp8": torch.float8_e4m3fn, "mxfp4": torch.uint8}.get(cfg.w_dtype, _TORCH_DT.get(cfg.w_dtype))
+    w13 = torch.empty((E, 2 * I, D // 2 if mx else D), dtype=wdt, device=dev)
+    w2 = torch.empty((E, D, I // 2 if mx else I), dtype=wdt, device=dev)
     fp8 = cfg.w_dtype == "fp8"
-    s13 = torch.empty((E, 2 * I), dtype=torch.float32, device=dev) if fp8 else None
-    s2 = torch.empty((E, D), dtype=torch.float32, device=dev) if fp8 else None
+    s13 = s2 = None
+    if fp8:
+        s13 = torch.empty((E, 2 * I), dtype=torch.float32, device=dev)
+        s2 = torch.empty((E, D), dtype=torch.float32, device=dev)
+    if mx:
+        s13 = torch.empty((E, D // 128, 2 * I, 4), dtype=torch.uint8, device=dev)
+        s2 = torch.empty((E, I // 128, D, 4), dtype=torch.uint8, device=dev)
     for e in range(E):
         a = torch.randn((2 * I, D), generator=gw, device=dev) / math.sqrt(D)
         q, s = _cast(a, cfg.w_dtype)
         w13[e].copy_(q)
-        if fp8:
+        if s is not None:
             s13[e].copy_(s)
         b = torch.randn((D, I), generator=gw, device=dev) / math.sqrt(I)
         q, s = _cast(b, cfg.w_dtype)
         w2[e].copy_(q)
-        if fp8:
+        if s is not None:
             s2[e].copy_(s)
     w13s = w2s = s13s = s2s = None
     if Is:
@@ -177,7 +223,7 @@ def to_bits(t: Optional[torch.Tensor]):
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float8_e4m3fn:
         return t.view(torch.uint8).numpy()
-    if t.dtype == torch.float32:
+    if t.dtype in (torch.float32, torch.uint8):
         return t.numpy()
     raise TypeError(f"unsupported dtype {t.dtype}")
 
