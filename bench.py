@@ -71,7 +71,7 @@ def copy_calib(mib: int):
     print(json.dumps({"copy_calib_bytes": n, "copies": 10}), flush=True)
 
 
-def cpu_baseline(wl, n_tokens: int, act_quant: bool = False):
+def cpu_baseline(wl, n_tokens: int, act_quant: int = 0):
     """Time the oracle (as it stands) on the first n_tokens tokens of the batch:
     routing of those tokens, every expert they touch, the shared branch and
     the combine, with expert weights decoded from their stored format inside
@@ -82,6 +82,7 @@ def cpu_baseline(wl, n_tokens: int, act_quant: bool = False):
     from oracle.actquant import layer_w8a8
     from oracle.formats import decode
     from oracle.moe import layer
+    from oracle.mx import decode_weight, layer_w4a8
     from workloads import host_expert, host_shared, to_bits
 
     c = wl.cfg
@@ -98,22 +99,24 @@ def cpu_baseline(wl, n_tokens: int, act_quant: bool = False):
 
     def expert(e):
         w13, s13, w2, s2 = raw[e]
-        return decode(w13, c.w_dtype), s13, decode(w2, c.w_dtype), s2
+        return (*decode_weight(w13, s13, c.w_dtype), *decode_weight(w2, s2, c.w_dtype))
 
     t0 = time.perf_counter()
     x = decode(xb, c.act_dtype)
     wr = decode(wrb, c.act_dtype)
     shared = None
     if sh is not None:
-        shared = (decode(sh[0], c.shared_w_dtype), sh[1], decode(sh[2], c.shared_w_dtype), sh[3])
-    (layer_w8a8 if act_quant else layer)(x, wr, c.k, expert, shared, c.act, c.act_shared)
+        shared = (*decode_weight(sh[0], sh[1], c.shared_w_dtype),
+                  *decode_weight(sh[2], sh[3], c.shared_w_dtype))
+    fn = {0: layer, 1: layer_w8a8, 2: layer_w4a8}[act_quant]
+    fn(x, wr, c.k, expert, shared, c.act, c.act_shared)
     dt = time.perf_counter() - t0
     threads = 1
     for info in threadpool_info():
         if info.get("user_api") == "blas":
             threads = max(threads, int(info.get("num_threads", 1)))
     return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"float64 NumPy oracle{' (W8A8)' if act_quant else ''}, whole layer on the "
+            "sample": (f"float64 NumPy oracle{['', ' (W8A8)', ' (W4A8)'][act_quant]}, whole layer on the "
                        f"first {n_tokens} of {c.T} tokens "
                        f"({len(used)} experts decoded from {c.w_dtype}), {dt:.1f} s")}
 
@@ -140,9 +143,11 @@ def main():
     torch.cuda.set_device(0)
     wl = generate(cfg, seed=0, weight_device="cuda")
     wl.x, wl.wr = wl.x.cuda(), wl.wr.cuda()
+    # MXFP4 weights always run with MXFP8 activations (W4A8)
+    aq = (B.MOE_ACT_QUANT_MXFP8 if cfg.w_dtype == "mxfp4"
+          else B.MOE_ACT_QUANT_FP8_ROW if args.act_quant else B.MOE_ACT_QUANT_NONE)
     p = B.make_problem(cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.act, cfg.act_shared,
-                       cfg.act_dtype, cfg.w_dtype, cfg.shared_w_dtype, args.policy,
-                       act_quant=B.MOE_ACT_QUANT_FP8_ROW if args.act_quant else 0)
+                       cfg.act_dtype, cfg.w_dtype, cfg.shared_w_dtype, args.policy, act_quant=aq)
     ws_bytes = B.moe_layer_workspace_size(p)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     y = torch.empty((cfg.T, cfg.D), dtype=wl.x.dtype, device="cuda")
@@ -205,12 +210,13 @@ def main():
     bytes_ /= launches_per_step
     flops /= launches_per_step
     ai = flops / bytes_ if bytes_ else 0.0
-    # the matrix cores' dtype: fp8 x fp8 with quantised activations
-    wdt = "fp8" if args.act_quant else ("bf16" if cfg.act_dtype == "bf16" else "f32")
+    # the matrix cores' dtype: fp8 x fp8 with quantised activations; e4m3 x
+    # e2m1 (W4A8) issues at the fp8 rate, so its peak is fp8's
+    wdt = "fp8" if aq else ("bf16" if cfg.act_dtype == "bf16" else "f32")
     ridge = cm.PEAK_TFLOPS[wdt] * 1e12 / (cm.PEAK_HBM_GBS * 1e9)
     traffic = None
     tpath = os.path.join(ROOT, "profiles",
-                         f"traffic_{name}_{cfg.name}{'_w8a8' if args.act_quant else ''}.json")
+                         f"traffic_{name}_{cfg.name}{'_w8a8' if aq == B.MOE_ACT_QUANT_FP8_ROW else ''}.json")
     if os.path.exists(tpath):
         tj = json.load(open(tpath))
         if tj.get("sources") and tj.get("sources_sha256") == sources_hash(tj["sources"]):
@@ -231,11 +237,11 @@ def main():
         "metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": wdt, "data": "synthetic",
+        "dtype": "fp8*fp4" if aq == B.MOE_ACT_QUANT_MXFP8 else wdt, "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "D": cfg.D, "E": cfg.E, "k": cfg.k,
                    "I": cfg.I, "I_shared": cfg.I_shared, "act": cfg.act,
                    "w_dtype": cfg.w_dtype, "touched_experts": touched, "policy": args.policy,
-                   "act_quant": "fp8_per_token" if args.act_quant else "none"},
+                   "act_quant": ["none", "fp8_per_token", "mxfp8"][aq]},
         "roofline": roof,
         "grouped_gemm": {
             "ms_per_step": gemm_ms,
@@ -248,7 +254,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         n = args.cpu_sample_tokens or {"qwen_decode": 64, "ling_decode": 16}.get(cfg.name, 16)
-        out["cpu_baseline"] = cpu_baseline(wl, min(n, cfg.T), args.act_quant)
+        out["cpu_baseline"] = cpu_baseline(wl, min(n, cfg.T), aq)
     print(json.dumps(out), flush=True)
 
 

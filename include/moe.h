@@ -29,9 +29,14 @@
  *    chunked product); W2[e] is [D, I].  fp8 weights carry fp32 per-output-
  *    channel scales s13[e][2I] and s2[e][D], applied after the reduction
  *    ("Ling-2.6-1T with SGLang-JAX" page, section 5, per-channel scaling).
- *  - Supported dtype combinations: {act F32, weights F32} and
+ *    MXFP4 weights carry E8M0 block scales in place of the per-channel ones:
+ *    s13[e] is uint8 [D/128][2I][4] and s2[e] uint8 [I/128][D][4] (for each
+ *    group of 128 K elements, each output row's four block scales side by
+ *    side).
+ *  - Supported dtype combinations: {act F32, weights F32},
  *    {act BF16, weights BF16 or FP8_E4M3FN}, the latter also with dynamic
- *    per-token fp8 activations (act_quant); anything else is
+ *    per-token fp8 activations (act_quant), and {act BF16, routed and shared
+ *    weights MXFP4_E2M1, act_quant MXFP8} (W4A8); anything else is
  *    MOE_ERR_UNSUPPORTED (no silent fallback).
  *  - Limits: 1 <= k <= min(E, 32); E <= 1024; D, I, I_shared multiples of 64;
  *    T*k and T*max(D, I) below 2^31.  T == 0 is valid and enqueues nothing.
@@ -50,6 +55,9 @@ extern "C" {
 #define MOE_F32         0
 #define MOE_BF16        1
 #define MOE_FP8_E4M3FN  2   /* OCP e4m3fn: bias 7, max 448, no inf, 0x7F/0xFF NaN */
+#define MOE_MXFP4_E2M1  3   /* weights only: OCP MXFP4, e2m1 codes two per byte
+                               (element 2j in the low nibble) with one E8M0
+                               scale 2^(e-127) per 32 consecutive K elements */
 
 /* gated activations of the expert FFN */
 #define MOE_ACT_SILU       0   /* SwiGLU: SiLU(gate) * up            */
@@ -63,6 +71,7 @@ extern "C" {
 /* activation quantisation of the expert GEMMs (moe_problem_t.act_quant) */
 #define MOE_ACT_QUANT_NONE     0   /* bf16 activations                       */
 #define MOE_ACT_QUANT_FP8_ROW  1   /* dynamic per-token fp8 (see below)      */
+#define MOE_ACT_QUANT_MXFP8    2   /* dynamic MXFP8 blocks (see below)       */
 
 typedef enum {
   MOE_OK = 0,
@@ -111,6 +120,17 @@ typedef struct moe_problem {
  *                         MOE_TILE_STREAM; routing and combine are unchanged.
  *                         Results differ from the exact layer by the
  *                         quantisation (a few per cent of the output range).
+ *  MOE_ACT_QUANT_MXFP8    W4A8 ("CANN Qwen3-MoE" page, high-throughput
+ *                         prefill: MXFP4 weights, activations quantised
+ *                         dynamically to MXFP8 before the grouped matmul):
+ *                         each GEMM input row (x; the stored bf16 h) is
+ *                         quantised as moe_quantize_rows_mx does, and the
+ *                         e4m3fn blocks and the MXFP4 weight blocks are
+ *                         multiplied on the scaled fp8/fp4 matrix cores with
+ *                         both block scales applied inside the product.
+ *                         Requires act BF16, MXFP4 routed and shared weights,
+ *                         D, I and I_shared multiples of 128 and a tile policy
+ *                         other than MOE_TILE_STREAM.
  */
 
 /*
@@ -166,21 +186,22 @@ moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_
  *   a         [*, D] act dtype: A_r = a[row_token[r]] if row_token, else a[r]
  *   row_token [rows] int32 or NULL
  *   offsets   [n_groups+1] int32 device array, offsets[n_groups] <= rows_upper_bound
- *   w13 [n_groups, 2I, D], w2 [n_groups, D, I] (w_dtype); s13 [n_groups, 2I],
- *   s2 [n_groups, D] fp32, required for fp8 and ignored otherwise
+ *   w13 [n_groups, 2I, D], w2 [n_groups, D, I] (w_dtype; MXFP4: D/2 and I/2
+ *   bytes per row); s13 [n_groups, 2I], s2 [n_groups, D] fp32 for fp8, the
+ *   E8M0 block scales for MXFP4 (layout above), ignored otherwise
  *   h   [rows_upper_bound, I] act dtype (written; intermediate)
  *   out [rows_upper_bound, D] act dtype (written)
  *   rows_upper_bound  host-known bound on offsets[n_groups]; it sizes the grid
  *   ws / ws_bytes     scratch of at least moe_grouped_ffn_workspace_size bytes
- *   With act_quant = MOE_ACT_QUANT_FP8_ROW the quantised copies of the A rows
- *   and of h (and their scales) live in the workspace; h is still written in
- *   bf16 (it is the stored value that gets quantised).
+ *   With act_quant the quantised copies of the A rows and of h (and their
+ *   scales) live in the workspace; h is still written in bf16 (it is the
+ *   stored value that gets quantised).
  */
 moe_status_t moe_grouped_ffn_workspace_size(const moe_problem_t* p, int32_t n_groups,
                                             int32_t rows_upper_bound, size_t* bytes);
 moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t rows_upper_bound,
                              const void* a, const int32_t* row_token, const int32_t* offsets,
-                             const void* w13, const float* s13, const void* w2, const float* s2,
+                             const void* w13, const void* s13, const void* w2, const void* s2,
                              void* h, void* out, void* ws, size_t ws_bytes, void* stream);
 
 /*
@@ -202,13 +223,13 @@ typedef struct moe_layer_args {
   const void* w_router;     /* [E, D] act dtype (unused with logits_in)  */
   const float* logits_in;   /* [T, E] fp32 or NULL                        */
   const void* w13;          /* [E, 2I, D]                                 */
-  const float* s13;         /* [E, 2I] (fp8 only)                         */
+  const void* s13;          /* [E, 2I] fp32 (fp8); E8M0 blocks (MXFP4)    */
   const void* w2;           /* [E, D, I]                                  */
-  const float* s2;          /* [E, D]  (fp8 only)                         */
+  const void* s2;           /* [E, D]  fp32 (fp8); E8M0 blocks (MXFP4)    */
   const void* w13_shared;   /* [2I_shared, D]  (NULL iff I_shared == 0)   */
-  const float* s13_shared;  /* [2I_shared]     (fp8 only)                 */
+  const void* s13_shared;   /* [2I_shared]     (fp8; MXFP4 blocks)        */
   const void* w2_shared;    /* [D, I_shared]                              */
-  const float* s2_shared;   /* [D]             (fp8 only)                 */
+  const void* s2_shared;    /* [D]             (fp8; MXFP4 blocks)        */
   void* y;                  /* [T, D] act dtype, written                  */
   float* logits_out;        /* [T, E] optional                            */
   int32_t* topk_idx_out;    /* [T, k] optional                            */
@@ -246,6 +267,25 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* args, voi
  */
 moe_status_t moe_quantize_rows(const void* a, int32_t rows, int32_t cols, int64_t lda, uint8_t* q,
                                float* scale, void* stream);
+
+/*
+ * moe_quantize_rows_mx -- dynamic MXFP8 quantisation, the activation side of
+ * the W4A8 decomposition ("CANN Qwen3-MoE" page, high-throughput prefill),
+ * with the block format of the OCP microscaling specification: each block of
+ * 32 consecutive elements of a row gets one E8M0 scale code
+ *   e = clamp(floor(log2(max |a|)) - 8, -127, 127) + 127   (8 = the largest
+ *       e4m3fn exponent; a block of zeros gets e = 0),
+ * and each element the e4m3fn code nearest to a / 2^(e-127) (exact power-of-
+ * two scaling), ties to the even code, magnitudes above 448 saturating.
+ *   a     [rows, lda] bf16 (the first cols columns are read); lda % 8 == 0
+ *   q     [rows, cols] uint8 (written)
+ *   scale uint8 [cols/128][rows][4] (written): the scale of block b of row r
+ *         at (b / 4) * rows * 4 + r * 4 + b % 4, the layout the W4A8 GEMM reads
+ *   cols % 128 == 0 and 0 < cols <= 16384, else MOE_ERR_SHAPE; a 16-byte and q
+ *   8-byte aligned.  Non-finite inputs are outside the contract.
+ */
+moe_status_t moe_quantize_rows_mx(const void* a, int32_t rows, int32_t cols, int64_t lda, uint8_t* q,
+                                  uint8_t* scale, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* moe_status_string(moe_status_t status);

@@ -15,14 +15,14 @@ from typing import Optional
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
-MOE_F32, MOE_BF16, MOE_FP8_E4M3FN = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_FP8_E4M3FN, MOE_MXFP4_E2M1 = 0, 1, 2, 3
 MOE_ACT_SILU, MOE_ACT_GELU_TANH = 0, 1
 MOE_TILE_AUTO, MOE_TILE_STREAM, MOE_TILE_LDS = 0, 1, 2
-MOE_ACT_QUANT_NONE, MOE_ACT_QUANT_FP8_ROW = 0, 1
+MOE_ACT_QUANT_NONE, MOE_ACT_QUANT_FP8_ROW, MOE_ACT_QUANT_MXFP8 = 0, 1, 2
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
 
-DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3FN}
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3FN, "mxfp4": MOE_MXFP4_E2M1}
 ACTS = {"silu": MOE_ACT_SILU, "gelu_tanh": MOE_ACT_GELU_TANH}
 POLICIES = {"auto": MOE_TILE_AUTO, "stream": MOE_TILE_STREAM, "lds": MOE_TILE_LDS}
 
@@ -72,6 +72,7 @@ _SIG = {
     "moe_stage_name": [ctypes.c_int32],
     "moe_debug_fp8_to_bf16": [_vp, _vp, ctypes.c_int32, _vp],
     "moe_quantize_rows": [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _vp, _vp, _vp],
+    "moe_quantize_rows_mx": [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _vp, _vp, _vp],
 }
 
 
@@ -220,6 +221,11 @@ def moe_timing_read():
 def moe_quantize_rows(a, rows: int, cols: int, lda: int, q, scale, stream=None):
     _check(lib().moe_quantize_rows(_p(a), rows, cols, lda, _p(q), _p(scale), _stream(stream)),
            "moe_quantize_rows")
+
+
+def moe_quantize_rows_mx(a, rows: int, cols: int, lda: int, q, scale, stream=None):
+    _check(lib().moe_quantize_rows_mx(_p(a), rows, cols, lda, _p(q), _p(scale), _stream(stream)),
+           "moe_quantize_rows_mx")
 
 
 def moe_debug_fp8_to_bf16(codes, out, n: int, stream=None):

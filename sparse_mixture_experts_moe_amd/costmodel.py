@@ -10,7 +10,18 @@ MI355X peaks used for rooflines are the vendor's dense figures.
 """
 from __future__ import annotations
 
-DTYPE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+DTYPE_BYTES = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5}
+
+
+def _scale_bytes(n_rows: int, K: int, w_dtype: str) -> float:
+    """Scales of an [n_rows, K] weight: fp32 per row (fp8), one E8M0 byte per
+    32 elements (MXFP4), none otherwise."""
+    if w_dtype == "fp8":
+        return 4.0 * n_rows
+    if w_dtype == "mxfp4":
+        return n_rows * K / 32.0
+    return 0.0
+
 
 # MI355X published dense peaks
 PEAK_HBM_GBS = 8000.0
@@ -36,25 +47,19 @@ def router_flops(T: int, D: int, E: int) -> float:
 
 
 def expert_weight_bytes(D: int, I: int, w_dtype: str, with_scales: bool = False) -> float:
-    """W13 (2I x D) + W2 (D x I) of one expert, plus fp32 per-channel scales."""
+    """W13 (2I x D) + W2 (D x I) of one expert, plus their scales."""
     b = 3.0 * D * I * DTYPE_BYTES[w_dtype]
     if with_scales:
-        b += 4.0 * (2 * I + D)
+        b += _scale_bytes(2 * I, D, w_dtype) + _scale_bytes(D, I, w_dtype)
     return b
 
 
 def w13_bytes(D: int, I: int, w_dtype: str) -> float:
-    b = 2.0 * I * D * DTYPE_BYTES[w_dtype]
-    if w_dtype == "fp8":
-        b += 4.0 * 2 * I
-    return b
+    return 2.0 * I * D * DTYPE_BYTES[w_dtype] + _scale_bytes(2 * I, D, w_dtype)
 
 
 def w2_bytes(D: int, I: int, w_dtype: str) -> float:
-    b = 1.0 * D * I * DTYPE_BYTES[w_dtype]
-    if w_dtype == "fp8":
-        b += 4.0 * D
-    return b
+    return 1.0 * D * I * DTYPE_BYTES[w_dtype] + _scale_bytes(D, I, w_dtype)
 
 
 def layer_flops(cfg) -> float:
@@ -75,12 +80,10 @@ def gemm_flops(cfg) -> float:
 def layer_bytes(cfg, touched_experts: int) -> float:
     """x + Wr + every touched expert's weights once (+scales) + shared + y."""
     a = DTYPE_BYTES[cfg.act_dtype]
-    fp8 = cfg.w_dtype == "fp8"
     b = cfg.T * cfg.D * a + cfg.E * cfg.D * a
-    b += touched_experts * expert_weight_bytes(cfg.D, cfg.I, cfg.w_dtype, fp8)
+    b += touched_experts * expert_weight_bytes(cfg.D, cfg.I, cfg.w_dtype, True)
     if cfg.I_shared:
-        b += expert_weight_bytes(cfg.D, cfg.I_shared, cfg.shared_w_dtype,
-                                 cfg.shared_w_dtype == "fp8")
+        b += expert_weight_bytes(cfg.D, cfg.I_shared, cfg.shared_w_dtype, True)
     b += cfg.T * cfg.D * a
     return b
 

@@ -93,6 +93,63 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   if (lane == 0) scale[r] = s;
 }
 
+// MXFP8: lane l's chunks l, l + 64, ...; the four chunks of a 32-element block
+// sit in four consecutive lanes, so a block's max is a butterfly over them.
+template <int NCH>
+__global__ __launch_bounds__(256) void quant_rows_mx_kernel(const uint16_t* __restrict__ a, int rows,
+                                                            int cols, int64_t lda, uint8_t* __restrict__ q,
+                                                            uint8_t* __restrict__ scale) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const uint16_t* row = a + r * lda;
+  const int nch = cols / 8;
+  uint8_t* qrow = q + r * cols;
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int c = lane + 64 * u;      // chunk; block c / 4 (uniform validity per block of 4 lanes)
+    const uint4 v = c < nch ? *reinterpret_cast<const uint4*>(row + 8 * c) : uint4{0, 0, 0, 0};
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      amax = fmaxf(amax, fabsf(__uint_as_float(w[j] << 16)));
+      amax = fmaxf(amax, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
+    }
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    // shared exponent floor(log2 amax) - 8 (e4m3fn's largest exponent), exact
+    int ex = -127;
+    if (amax > 0.f) {
+      int e2;
+      (void)frexpf(amax, &e2);        // amax = m * 2^e2, m in [0.5, 1)
+      ex = min(127, max(-127, e2 - 1 - 8));
+    }
+    if (c >= nch) continue;
+    uint32_t packed[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x0 = ldexpf(__uint_as_float(w[j] << 16), -ex);
+      const float x1 = ldexpf(__uint_as_float(w[j] & 0xFFFF0000u), -ex);
+      const uint32_t pair = e4m3_code(fminf(fmaxf(x0, -448.0f), 448.0f)) |
+                            (e4m3_code(fminf(fmaxf(x1, -448.0f), 448.0f)) << 8);
+      packed[j >> 1] |= pair << (16 * (j & 1));
+    }
+    *reinterpret_cast<uint2*>(qrow + 8 * c) = uint2{packed[0], packed[1]};
+    if ((lane & 3) == 0) {
+      const int blk = c / 4;
+      scale[(static_cast<int64_t>(blk / 4) * rows + r) * 4 + (blk % 4)] = static_cast<uint8_t>(ex + 127);
+    }
+  }
+}
+
+template <int NCH>
+hipError_t go_mx(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q, uint8_t* scale,
+                 hipStream_t s) {
+  quant_rows_mx_kernel<NCH><<<(rows + 3) / 4, 256, 0, s>>>(a, rows, cols, lda, q, scale);
+  return hipGetLastError();
+}
+
 template <int NCH>
 hipError_t go(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q, float* scale,
               hipStream_t s) {
@@ -116,6 +173,20 @@ hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, int64_t lda,
   if (nch <= 8) return go<8>(a, rows, cols, lda, q, scale, s);
   if (nch <= 16) return go<16>(a, rows, cols, lda, q, scale, s);
   return go<32>(a, rows, cols, lda, q, scale, s);
+}
+
+hipError_t launch_quant_rows_mx(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q,
+                                uint8_t* scale, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (rows < 0 || cols <= 0 || cols % 128 || cols > QMAX || lda < cols || lda % 8) return hipErrorInvalidValue;
+  if (reinterpret_cast<uintptr_t>(a) % 16 || reinterpret_cast<uintptr_t>(q) % 8) return hipErrorInvalidValue;
+  const int nch = (cols / 8 + 63) / 64;
+  if (nch <= 1) return go_mx<1>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 2) return go_mx<2>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 4) return go_mx<4>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 8) return go_mx<8>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 16) return go_mx<16>(a, rows, cols, lda, q, scale, s);
+  return go_mx<32>(a, rows, cols, lda, q, scale, s);
 }
 
 }  // namespace moe

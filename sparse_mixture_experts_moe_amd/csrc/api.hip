@@ -19,12 +19,59 @@ size_t dt_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
 
 bool act_ok(int a) { return a == MOE_ACT_SILU || a == MOE_ACT_GELU_TANH; }
 bool dt_ok(int d) { return d == MOE_F32 || d == MOE_BF16 || d == MOE_FP8_E4M3FN; }
+bool wdt_ok(int d) { return dt_ok(d) || d == MOE_MXFP4_E2M1; }
 
 bool combo_ok(int act_dt, int w_dt) {
   if (act_dt == MOE_F32) return w_dt == MOE_F32;
-  if (act_dt == MOE_BF16) return w_dt == MOE_BF16 || w_dt == MOE_FP8_E4M3FN;
+  if (act_dt == MOE_BF16) return w_dt == MOE_BF16 || w_dt == MOE_FP8_E4M3FN || w_dt == MOE_MXFP4_E2M1;
   return false;
 }
+
+bool quantised(const moe_problem_t* p) { return p->act_quant != MOE_ACT_QUANT_NONE; }
+
+// Bytes of the activation scales of `rows` quantised rows of `cols` columns:
+// one fp32 per row, or (MXFP8) one E8M0 byte per 32 columns.
+size_t qscale_bytes(const moe_problem_t* p, int64_t rows, int64_t cols) {
+  return static_cast<size_t>(p->act_quant == MOE_ACT_QUANT_MXFP8 ? rows * (cols / 32) : rows * 4);
+}
+
+// Device dtype of the expert GEMMs' activations.
+int gemm_a_dtype(const moe_problem_t* p) {
+  return p->act_quant == MOE_ACT_QUANT_FP8_ROW ? DT_FP8
+         : p->act_quant == MOE_ACT_QUANT_MXFP8 ? DT_MXFP8 : p->act_dtype;
+}
+
+// Quantise `rows` bf16 rows with the problem's activation quantisation.
+hipError_t quant_rows(const moe_problem_t* p, const void* a, int rows, int cols, uint8_t* q,
+                      void* scale, hipStream_t s) {
+  if (p->act_quant == MOE_ACT_QUANT_MXFP8)
+    return launch_quant_rows_mx(static_cast<const uint16_t*>(a), rows, cols, cols, q,
+                                static_cast<uint8_t*>(scale), s);
+  return launch_quant_rows(static_cast<const uint16_t*>(a), rows, cols, cols, q,
+                           static_cast<float*>(scale), s);
+}
+
+// Point a GEMM set's activation and weight scales at the right buffers.
+void set_scales(const moe_problem_t* p, GSet& S, const void* a_scale, int32_t a_scale_rows,
+                const void* w_scale, int w_dtype, int64_t w_scale_gstride_bytes) {
+  S.a_scale = nullptr;
+  S.a_mx = nullptr;
+  S.w_mx = nullptr;
+  S.scale = nullptr;
+  if (p->act_quant == MOE_ACT_QUANT_FP8_ROW) S.a_scale = static_cast<const float*>(a_scale);
+  if (p->act_quant == MOE_ACT_QUANT_MXFP8) {
+    S.a_mx = static_cast<const uint8_t*>(a_scale);
+    S.a_mx_rows = a_scale_rows;
+  }
+  if (w_dtype == MOE_FP8_E4M3FN) S.scale = static_cast<const float*>(w_scale);
+  if (w_dtype == MOE_MXFP4_E2M1) {
+    S.w_mx = static_cast<const uint8_t*>(w_scale);
+    S.w_mx_gstride = w_scale_gstride_bytes;
+  }
+}
+
+// weights that need a scale argument
+bool w_scaled(int w_dtype) { return w_dtype == MOE_FP8_E4M3FN || w_dtype == MOE_MXFP4_E2M1; }
 
 // Checks common to every entry point.
 moe_status_t check_problem(const moe_problem_t* p, bool need_ffn, bool need_router) {
@@ -36,7 +83,7 @@ moe_status_t check_problem(const moe_problem_t* p, bool need_ffn, bool need_rout
   const int64_t Tk = static_cast<int64_t>(p->T) * std::max(p->k, 1);
   const int64_t wide = std::max<int64_t>({p->D, p->I, p->I_shared, p->E});
   if (Tk >= (int64_t(1) << 31) || (Tk + p->T) * wide >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
-  if (!dt_ok(p->act_dtype) || !dt_ok(p->w_dtype) || !dt_ok(p->shared_w_dtype)) return MOE_ERR_DTYPE;
+  if (!dt_ok(p->act_dtype) || !wdt_ok(p->w_dtype) || !wdt_ok(p->shared_w_dtype)) return MOE_ERR_DTYPE;
   if (!act_ok(p->act) || !act_ok(p->act_shared)) return MOE_ERR_DTYPE;
   if (p->tile_policy < MOE_TILE_AUTO || p->tile_policy > MOE_TILE_LDS) return MOE_ERR_DTYPE;
   if (p->act_dtype == MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
@@ -44,11 +91,18 @@ moe_status_t check_problem(const moe_problem_t* p, bool need_ffn, bool need_rout
   if (need_ffn && p->I_shared && !combo_ok(p->act_dtype, p->shared_w_dtype))
     return MOE_ERR_UNSUPPORTED;
   if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_UNSUPPORTED;
-  if (p->act_quant != MOE_ACT_QUANT_NONE && p->act_quant != MOE_ACT_QUANT_FP8_ROW) return MOE_ERR_UNSUPPORTED;
-  if (need_ffn && p->act_quant == MOE_ACT_QUANT_FP8_ROW) {
-    // fp8 x fp8 runs on the tiled kernel only, with fp8 weights on both branches
-    if (p->act_dtype != MOE_BF16 || p->w_dtype != MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
-    if (p->I_shared && p->shared_w_dtype != MOE_FP8_E4M3FN) return MOE_ERR_UNSUPPORTED;
+  if (p->act_quant < MOE_ACT_QUANT_NONE || p->act_quant > MOE_ACT_QUANT_MXFP8) return MOE_ERR_UNSUPPORTED;
+  // MXFP4 weights go with MXFP8 activations and nothing else, on both branches
+  const bool mx = p->act_quant == MOE_ACT_QUANT_MXFP8;
+  if (need_ffn && (mx != (p->w_dtype == MOE_MXFP4_E2M1) ||
+                   (p->I_shared && mx != (p->shared_w_dtype == MOE_MXFP4_E2M1))))
+    return MOE_ERR_UNSUPPORTED;
+  if (need_ffn && quantised(p)) {
+    // fp8 x fp8 and MXFP8 x MXFP4 run on the tiled kernel only, with one
+    // weight format on both branches
+    const int wdt = mx ? MOE_MXFP4_E2M1 : MOE_FP8_E4M3FN;
+    if (p->act_dtype != MOE_BF16 || p->w_dtype != wdt) return MOE_ERR_UNSUPPORTED;
+    if (p->I_shared && p->shared_w_dtype != wdt) return MOE_ERR_UNSUPPORTED;
     if (p->tile_policy == MOE_TILE_STREAM) return MOE_ERR_UNSUPPORTED;
     const int km = tiled_k_multiple_a8();
     if (p->D % km || p->I % km || p->I_shared % km) return MOE_ERR_UNSUPPORTED;
@@ -98,8 +152,8 @@ bool tiled_fits(const moe_problem_t* p) {
 }
 
 Plan make_plan(const moe_problem_t* p, double mean_rows) {
-  if (p->act_quant == MOE_ACT_QUANT_FP8_ROW) {
-    // fp8 x fp8: the tiled kernel's one-block-per-CU shapes
+  if (quantised(p)) {
+    // fp8 x fp8, MXFP8 x MXFP4: the tiled kernel's one-block-per-CU shapes
     const int shape = mean_rows <= MOE_TALL_MEAN ? TILED_TALL : TILED_WIDE;
     return Plan{true, 0, tiled_bm(shape), shape};
   }
@@ -180,7 +234,7 @@ int router_splits(const moe_problem_t* p, const Plan& pl) {
 hipError_t run_gemm(const GArgs& g, const Plan& pl, bool gated, int a_dt, int w_dt, int o_dt,
                     hipStream_t s) {
   if (pl.tiled) return launch_tiled_gemm(g, g.shape, gated, w_dt, o_dt, a_dt, s);
-  if (a_dt == DT_FP8) return hipErrorInvalidValue;
+  if (a_dt == DT_FP8 || a_dt == DT_MXFP8) return hipErrorInvalidValue;
   return launch_stream_gemm(g, pl.mt, gated, a_dt, w_dt, o_dt, s);
 }
 
@@ -255,7 +309,7 @@ struct Carve {
 struct LayerLayout {
   size_t logits, idx, w, counts, offsets, row_token, row_of_slot, blk, rank, tiles, ntiles;
   size_t h, h_sh, o, o_sh, total;
-  size_t xq, sx, hq, sh, hsq, shs;   // fp8 activations and their row scales (act_quant)
+  size_t xq, sx, hq, sh, hsq, shs;   // quantised activations and their scales (act_quant)
   int tile_ub;
   int splits;
   Plan plan;
@@ -284,13 +338,13 @@ LayerLayout layer_layout(const moe_problem_t* p) {
   L.h_sh = c.take(T * p->I_shared * a);
   L.o = c.take(Tk * p->D * a);
   L.o_sh = c.take(p->I_shared ? T * p->D * a : 0);
-  if (p->act_quant == MOE_ACT_QUANT_FP8_ROW) {
+  if (quantised(p)) {
     L.xq = c.take(T * p->D);
-    L.sx = c.take(T * 4);
+    L.sx = c.take(qscale_bytes(p, T, p->D));
     L.hq = c.take(Tk * p->I);
-    L.sh = c.take(Tk * 4);
+    L.sh = c.take(qscale_bytes(p, Tk, p->I));
     L.hsq = c.take(T * p->I_shared);
-    L.shs = c.take(T * 4);
+    L.shs = c.take(qscale_bytes(p, T, p->I_shared));
   }
   L.total = c.off;
   return L;
@@ -318,12 +372,12 @@ FfnLayout ffn_layout(const moe_problem_t* p, const Plan& pl, int n_groups, int r
   Carve c;
   L.tiles = c.take(static_cast<size_t>(routed_tile_ub(rows_ub, n_groups, pl.bm)) * sizeof(GTile));
   L.ntiles = c.take(16);
-  if (p->act_quant == MOE_ACT_QUANT_FP8_ROW) {
-    const size_t a_rows = static_cast<size_t>(std::max(p->T, rows_ub));
-    L.aq = c.take(a_rows * p->D);
-    L.sa = c.take(a_rows * 4);
+  if (quantised(p)) {
+    const int64_t a_rows = std::max(p->T, rows_ub);
+    L.aq = c.take(static_cast<size_t>(a_rows) * p->D);
+    L.sa = c.take(qscale_bytes(p, a_rows, p->D));
     L.hq = c.take(static_cast<size_t>(rows_ub) * p->I);
-    L.sh = c.take(static_cast<size_t>(rows_ub) * 4);
+    L.sh = c.take(qscale_bytes(p, rows_ub, p->I));
   }
   L.total = c.off;
   return L;
@@ -436,13 +490,13 @@ moe_status_t moe_grouped_ffn_workspace_size(const moe_problem_t* p, int32_t n_gr
 
 moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t rows_upper_bound,
                              const void* a, const int32_t* row_token, const int32_t* offsets,
-                             const void* w13, const float* s13, const void* w2, const float* s2,
+                             const void* w13, const void* s13, const void* w2, const void* s2,
                              void* h, void* out, void* ws, size_t ws_bytes, void* stream) {
   size_t need = 0;
   moe_status_t st = moe_grouped_ffn_workspace_size(p, n_groups, rows_upper_bound, &need);
   if (st != MOE_OK) return st;
   if (!a || !offsets || !w13 || !w2 || !h || !out || !ws) return MOE_ERR_NULL;
-  if (p->w_dtype == MOE_FP8_E4M3FN && (!s13 || !s2)) return MOE_ERR_NULL;
+  if (w_scaled(p->w_dtype) && (!s13 || !s2)) return MOE_ERR_NULL;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (rows_upper_bound == 0) return MOE_OK;
   const Plan pl = make_plan(p, static_cast<double>(rows_upper_bound) / n_groups);
@@ -452,18 +506,17 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t r
   GTile* tiles = reinterpret_cast<GTile*>(w + FL.tiles);
   int32_t* ntiles = reinterpret_cast<int32_t*>(w + FL.ntiles);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const bool fp8 = p->w_dtype == MOE_FP8_E4M3FN;
-  const bool aq = p->act_quant == MOE_ACT_QUANT_FP8_ROW;
-  const int a_dt = aq ? DT_FP8 : p->act_dtype;
+  const bool aq = quantised(p);
+  const int a_dt = gemm_a_dtype(p);
   const int a_rows = row_token ? p->T : rows_upper_bound;
   if (row_token && p->T <= 0) return MOE_ERR_SHAPE;
   uint8_t* aq8 = reinterpret_cast<uint8_t*>(w + FL.aq);
-  float* sa = reinterpret_cast<float*>(w + FL.sa);
+  void* sa = w + FL.sa;
   uint8_t* hq = reinterpret_cast<uint8_t*>(w + FL.hq);
-  float* sh = reinterpret_cast<float*>(w + FL.sh);
+  void* sh = w + FL.sh;
   if (aq) {
     StageScope sc(ST_QUANT, s);
-    MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(a), a_rows, p->D, p->D, aq8, sa, s));
+    MOE_LAUNCH(quant_rows(p, a, a_rows, p->D, aq8, sa, s));
   }
   {
     StageScope sc(ST_TILES, s);
@@ -477,11 +530,10 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t r
     S.K = p->D;
     S.a_rows = a_rows;
     S.a = aq ? static_cast<const void*>(aq8) : a;
-    S.a_scale = aq ? sa : nullptr;
     S.gather = row_token;
     S.lda = p->D;
     S.w = w13;
-    S.scale = fp8 ? s13 : nullptr;
+    set_scales(p, S, sa, a_rows, s13, p->w_dtype, static_cast<int64_t>(p->D / 128) * 2 * p->I * 4);
     S.w_gstride = static_cast<int64_t>(2) * p->I * p->D;
     S.s_gstride = 2 * p->I;
     S.NB = 2 * p->I;
@@ -500,11 +552,10 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t r
     S.K = p->I;
     S.a_rows = rows_upper_bound;
     S.a = aq ? static_cast<void*>(hq) : h;
-    S.a_scale = aq ? sh : nullptr;
     S.gather = nullptr;
     S.lda = p->I;
     S.w = w2;
-    S.scale = fp8 ? s2 : nullptr;
+    set_scales(p, S, sh, rows_upper_bound, s2, p->w_dtype, static_cast<int64_t>(p->I / 128) * p->D * 4);
     S.w_gstride = static_cast<int64_t>(p->D) * p->I;
     S.s_gstride = p->D;
     S.NB = p->D;
@@ -519,7 +570,7 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t r
   }
   if (aq) {
     StageScope sc(ST_QUANT, s);
-    MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(h), rows_upper_bound, p->I, p->I, hq, sh, s));
+    MOE_LAUNCH(quant_rows(p, h, rows_upper_bound, p->I, hq, sh, s));
   }
   {
     StageScope sc(ST_FFN2, s);
@@ -556,10 +607,10 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
   if (st != MOE_OK) return st;
   if (!A || !A->x || !A->w13 || !A->w2 || !A->y) return MOE_ERR_NULL;
   if (!A->logits_in && !A->w_router) return MOE_ERR_NULL;
-  if (p->w_dtype == MOE_FP8_E4M3FN && (!A->s13 || !A->s2)) return MOE_ERR_NULL;
+  if (w_scaled(p->w_dtype) && (!A->s13 || !A->s2)) return MOE_ERR_NULL;
   if (p->I_shared) {
     if (!A->w13_shared || !A->w2_shared) return MOE_ERR_NULL;
-    if (p->shared_w_dtype == MOE_FP8_E4M3FN && (!A->s13_shared || !A->s2_shared)) return MOE_ERR_NULL;
+    if (w_scaled(p->shared_w_dtype) && (!A->s13_shared || !A->s2_shared)) return MOE_ERR_NULL;
   }
   const LayerLayout L = layer_layout(p);
   if (!ws) return MOE_ERR_NULL;
@@ -621,20 +672,18 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     }
   }
   // 3. grouped FFN: shared branch (dense rows) and routed experts in the same launches
-  const bool fp8 = p->w_dtype == MOE_FP8_E4M3FN;
-  const bool fp8s = p->shared_w_dtype == MOE_FP8_E4M3FN;
-  // fp8 activations: x quantised per token once, h per row after the gate/up GEMM
-  const bool aq = p->act_quant == MOE_ACT_QUANT_FP8_ROW;
-  const int a_dt = aq ? DT_FP8 : p->act_dtype;
+  // quantised activations: x quantised once, h per row after the gate/up GEMM
+  const bool aq = quantised(p);
+  const int a_dt = gemm_a_dtype(p);
   uint8_t* xq = reinterpret_cast<uint8_t*>(w + L.xq);
-  float* sx = reinterpret_cast<float*>(w + L.sx);
+  void* sx = w + L.sx;
   uint8_t* hq = reinterpret_cast<uint8_t*>(w + L.hq);
-  float* sh = reinterpret_cast<float*>(w + L.sh);
+  void* sh = w + L.sh;
   uint8_t* hsq = reinterpret_cast<uint8_t*>(w + L.hsq);
-  float* shs = reinterpret_cast<float*>(w + L.shs);
+  void* shs = w + L.shs;
   if (aq) {
     StageScope sc(ST_QUANT, s);
-    MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(A->x), p->T, p->D, p->D, xq, sx, s));
+    MOE_LAUNCH(quant_rows(p, A->x, p->T, p->D, xq, sx, s));
   }
   GArgs g1{};
   int si = 0;
@@ -643,10 +692,9 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     S.K = p->D;
     S.a_rows = p->T;
     S.a = aq ? static_cast<const void*>(xq) : A->x;
-    S.a_scale = aq ? sx : nullptr;
     S.lda = p->D;
     S.w = A->w13_shared;
-    S.scale = fp8s ? A->s13_shared : nullptr;
+    set_scales(p, S, sx, p->T, A->s13_shared, p->shared_w_dtype, 0);
     S.NB = 2 * p->I_shared;
     S.n_out = p->I_shared;
     S.act = p->act_shared;
@@ -660,11 +708,10 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     S.K = p->D;
     S.a_rows = p->T;
     S.a = aq ? static_cast<const void*>(xq) : A->x;
-    S.a_scale = aq ? sx : nullptr;
     S.gather = row_token;
     S.lda = p->D;
     S.w = A->w13;
-    S.scale = fp8 ? A->s13 : nullptr;
+    set_scales(p, S, sx, p->T, A->s13, p->w_dtype, static_cast<int64_t>(p->D / 128) * 2 * p->I * 4);
     S.w_gstride = static_cast<int64_t>(2) * p->I * p->D;
     S.s_gstride = 2 * p->I;
     S.NB = 2 * p->I;
@@ -685,10 +732,9 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     S.K = p->I_shared;
     S.a_rows = p->T;
     S.a = aq ? static_cast<void*>(hsq) : h_sh;
-    S.a_scale = aq ? shs : nullptr;
     S.lda = p->I_shared;
     S.w = A->w2_shared;
-    S.scale = fp8s ? A->s2_shared : nullptr;
+    set_scales(p, S, shs, p->T, A->s2_shared, p->shared_w_dtype, 0);
     S.NB = p->D;
     S.n_out = p->D;
     S.out = o_sh;
@@ -699,11 +745,10 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     S.K = p->I;
     S.a_rows = static_cast<int32_t>(Tk);
     S.a = aq ? static_cast<void*>(hq) : h;
-    S.a_scale = aq ? sh : nullptr;
     S.gather = nullptr;
     S.lda = p->I;
     S.w = A->w2;
-    S.scale = fp8 ? A->s2 : nullptr;
+    set_scales(p, S, sh, static_cast<int32_t>(Tk), A->s2, p->w_dtype, static_cast<int64_t>(p->I / 128) * p->D * 4);
     S.w_gstride = static_cast<int64_t>(p->D) * p->I;
     S.s_gstride = p->D;
     S.NB = p->D;
@@ -712,7 +757,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     S.ldo = p->D;
   }
   finish_grid(g2, pl, false);
-  if (fp8 != fp8s && p->I_shared) {
+  if (p->w_dtype != p->shared_w_dtype && p->I_shared) {
     // one launch covers one weight dtype: run the two sets separately
     for (int i = 0; i < 2; ++i) {
       GArgs a1{}, a2{};
@@ -738,11 +783,8 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     }
     if (aq) {
       StageScope sc(ST_QUANT, s);
-      MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(h), static_cast<int>(Tk), p->I, p->I,
-                                   hq, sh, s));
-      if (p->I_shared)
-        MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(h_sh), p->T, p->I_shared,
-                                     p->I_shared, hsq, shs, s));
+      MOE_LAUNCH(quant_rows(p, h, static_cast<int>(Tk), p->I, hq, sh, s));
+      if (p->I_shared) MOE_LAUNCH(quant_rows(p, h_sh, p->T, p->I_shared, hsq, shs, s));
     }
     {
       StageScope sc(ST_FFN2, s);
@@ -768,6 +810,19 @@ moe_status_t moe_quantize_rows(const void* a, int32_t rows, int32_t cols, int64_
   hipStream_t s = static_cast<hipStream_t>(stream);
   StageScope sc(ST_QUANT, s);
   MOE_LAUNCH(launch_quant_rows(static_cast<const uint16_t*>(a), rows, cols, lda, q, scale, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_quantize_rows_mx(const void* a, int32_t rows, int32_t cols, int64_t lda, uint8_t* q,
+                                  uint8_t* scale, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 128 || cols > quant_max_cols() || lda < cols || lda % 8)
+    return MOE_ERR_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!a || !q || !scale) return MOE_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(a) % 16 || reinterpret_cast<uintptr_t>(q) % 8) return MOE_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageScope sc(ST_QUANT, s);
+  MOE_LAUNCH(launch_quant_rows_mx(static_cast<const uint16_t*>(a), rows, cols, lda, q, scale, s));
   return MOE_OK;
 }
 

@@ -65,9 +65,11 @@ constexpr int KS = 32;                    // K elements per MFMA sub-step
 #endif
 constexpr int LDS_CU = 160 * 1024;        // LDS per CU
 
-template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8, int BK_, int MF_, bool A8_ = false>
+template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8, int BK_, int MF_, bool A8_ = false,
+          bool W4_ = false>
 struct Cfg {
   static constexpr bool A8 = A8_;                     // fp8 activations (with fp8 weights)
+  static constexpr bool W4 = W4_;                     // MXFP4 weights, MXFP8 activations (with A8)
   static constexpr int MF = MF_;                      // MFMA tile: 16 (16x16x32) or 32 (32x32x16 / x64 fp8)
   static constexpr int BK = BK_;                      // K elements per stage
   static constexpr int KSUB = A8 ? 64 : KS;           // K elements per MFMA sub-step
@@ -85,8 +87,16 @@ struct Cfg {
   static constexpr int WF = BNW / WN / MF;            // MF-weight-row fragments per wavefront
   static constexpr int WPE = NW * BPC / 4;            // wavefronts per SIMD
   static constexpr int A_BYTES = BM * ROWA;
-  static constexpr int B_BYTES = BNW * (FP8 ? ROWB8 : ROWB);
-  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int ROWBW = W4 ? BK / 2 : FP8 ? ROWB8 : ROWB;   // LDS bytes per weight tile row
+  static constexpr int B_BYTES = BNW * ROWBW;
+  // MX block scales of a stage, 4 bytes per row ([row][block]): activation
+  // rows one 4-byte copy per lane (gathered rows), weight rows 16 bytes (four
+  // consecutive rows) per lane
+  static constexpr int ASC_BYTES = W4 ? BM * 4 : 0;
+  static constexpr int BSC_BYTES = W4 ? BNW * 4 : 0;
+  static constexpr int ASC_I = ASC_BYTES / 256, BSC_I = BSC_BYTES / 1024;
+  static constexpr int NSC = ASC_I + BSC_I;           // scale copy instructions (one per wavefront)
+  static constexpr int STAGE = A_BYTES + B_BYTES + ASC_BYTES + BSC_BYTES;
   static constexpr int S0 = LDS_CU / BPC / STAGE;
   static constexpr int S = S0 > 6 ? 6 : S0;           // LDS ring depth
   static constexpr int LDS = S * STAGE;
@@ -100,6 +110,8 @@ struct Cfg {
   static_assert(TF * WF * MF * MF / 64 * WPE <= 256, "accumulators fit the AGPRs");
   static_assert(WPE == 1 || WPE == 2, "one or two wavefronts per SIMD");
   static_assert(!A8 || (FP8 && MF == 32), "fp8 activations: fp8 weights, 32x32x64 MFMAs");
+  static_assert(!W4 || (A8 && BK == 128), "MX weights: fp8 activations, 128-deep stages");
+  static_assert(ASC_I * 256 == ASC_BYTES && BSC_I * 1024 == BSC_BYTES && NSC <= NW, "scale copies");
 };
 
 // position of 16-byte chunk c in a tile row of RB bytes (an involution in c):
@@ -124,6 +136,17 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, const vo
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
   const uint64_t bs = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bs), "s"(l)
+               : "memory", "m0");
+}
+// Same with 4 bytes per lane (to lds + 4 * lane).
+__device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, const void* lds) {
+  const uint32_t l = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds))));
+  const uint64_t b = reinterpret_cast<uint64_t>(sbase);
+  const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
+  const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
+  const uint64_t bs = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(bs), "s"(l)
                : "memory", "m0");
 }
 #pragma clang diagnostic pop
@@ -269,13 +292,16 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
     }
     a_off[i] = static_cast<uint32_t>(arow * Sg.lda * (A8 ? 1 : 2) + c * 16);
   }
-  const char* b_base = uniform_ptr(static_cast<const char*>(Sg.w) +
-                                   (group * Sg.w_gstride + k_beg) * (FP8 ? 1 : 2));
+  // weight bytes of e elements
+  auto wbytes = [&](int64_t e) __attribute__((always_inline)) -> int64_t {
+    return C::W4 ? e / 2 : FP8 ? e : 2 * e;
+  };
+  const char* b_base = uniform_ptr(static_cast<const char*>(Sg.w) + wbytes(group * Sg.w_gstride + k_beg));
   uint32_t b_off[C::BL];
 #pragma unroll
   for (int i = 0; i < C::BL; ++i) {
     const int j = wave * C::BL + i;
-    constexpr int RB = FP8 ? ROWB8 : ROWB, LPR = RB / 16;
+    constexpr int RB = C::ROWBW, LPR = RB / 16;
     const int tr = (64 / LPR) * j + lane / LPR;
     const int c = upos<RB>(tr, lane % LPR);
     int wrow;
@@ -285,7 +311,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
     } else {
       wrow = n0 + tr < n_out ? n0 + tr : 0;
     }
-    b_off[i] = static_cast<uint32_t>((static_cast<int64_t>(wrow) * K * (FP8 ? 1 : 2)) + c * 16);
+    b_off[i] = static_cast<uint32_t>(wbytes(static_cast<int64_t>(wrow) * K) + c * 16);
   }
   // copy instruction k (0..P-1) of stage st: the A instructions, then B
   auto issue_one = [&](int st, int k) __attribute__((always_inline)) {
@@ -294,8 +320,61 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
       dma16(a_off[k], a_base + st * ROWA, base + (wave * C::AL + k) * 1024);
     } else {
       const int i = k - C::AL;
-      dma16(b_off[i], b_base + st * (FP8 ? ROWB8 : ROWB),
+      dma16(b_off[i], b_base + st * C::ROWBW,
             base + C::A_BYTES + (wave * C::BL + i) * 1024);
+    }
+  };
+  // MX block scales: wavefront w < NSC copies one part of stage st's scales --
+  // the 4 bytes of each of 64 activation rows, or 256 weight rows (4 rows per
+  // lane; gate and up rows each contiguous, 4 | n_out).
+  [[maybe_unused]] uint32_t sc_off = 0;
+  [[maybe_unused]] const char* sc_base = nullptr;
+  [[maybe_unused]] int64_t sc_stride = 0;   // bytes between consecutive 128-deep K groups
+  if constexpr (C::W4) {
+    const int kg0 = k_beg / 128;
+    if (wave < C::ASC_I) {
+      const int tr = 64 * wave + lane;
+      const int r = row0 + tr;
+      int64_t arow = 0;
+      if (r < row1) {
+        arow = Sg.gather ? Sg.gather[r] : r;
+        if (static_cast<uint64_t>(arow) >= static_cast<uint64_t>(Sg.a_rows)) arow = 0;
+      }
+      sc_off = static_cast<uint32_t>(arow * 4);
+      sc_stride = static_cast<int64_t>(Sg.a_mx_rows) * 4;
+      sc_base = uniform_ptr(reinterpret_cast<const char*>(Sg.a_mx) + kg0 * sc_stride);
+    } else if (wave < C::NSC) {
+      const int tr = 256 * (wave - C::ASC_I) + 4 * lane;   // first of the lane's 4 tile rows
+      int wrow;
+      if (GATED) {
+        const int n = n0 + (tr & (BNW / 2 - 1));
+        wrow = n < n_out ? (tr < BNW / 2 ? 0 : n_out) + n : 0;
+      } else {
+        wrow = n0 + tr < n_out ? n0 + tr : 0;
+      }
+      sc_off = static_cast<uint32_t>(wrow * 4);
+      sc_stride = static_cast<int64_t>(Sg.NB) * 4;
+      sc_base = uniform_ptr(reinterpret_cast<const char*>(Sg.w_mx) + group * Sg.w_mx_gstride + kg0 * sc_stride);
+    }
+  }
+  auto issue_scales = [&](int st) __attribute__((always_inline)) {
+    if constexpr (C::W4) {
+      char* sc_lds = smem + (st % S) * C::STAGE + C::A_BYTES + C::B_BYTES;
+      if (wave < C::ASC_I)
+        dma4(sc_off, sc_base + st * sc_stride, sc_lds + wave * 256);
+      else if (wave < C::NSC)
+        dma16(sc_off, sc_base + st * sc_stride, sc_lds + C::ASC_BYTES + (wave - C::ASC_I) * 1024);
+    }
+  };
+  // Waits for copies: this wavefront issues P copies per stage, plus one scale
+  // copy if it is a scale copier.
+  auto wait_stages = [&](int newer, auto m) __attribute__((always_inline)) {
+    constexpr int M = decltype(m)::value;
+    if constexpr (C::W4) {
+      if (wave < C::NSC) wait_newer<P + 1, M>(newer);
+      else wait_newer<P, M>(newer);
+    } else {
+      wait_newer<P, M>(newer);
     }
   };
 
@@ -330,7 +409,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
     i32x8 a[TF];
     i32x8 b[WF];
   };
-  using Frag = typename std::conditional<A8, Frag8, FragW>::type;
+  struct Frag4 {     // MXFP8 activations, MXFP4 weights, and the lane's block scales
+    i32x8 a[TF];
+    u32x4 b[WF];
+    int sa[TF];
+    int sb[WF];
+  };
+  using Frag = typename std::conditional<C::W4, Frag4, typename std::conditional<A8, Frag8, FragW>::type>::type;
   // 16-byte chunk (of the tile row) holding the lane's K elements of sub-step
   // h of a stage, in MFMA ks
   auto chunk_of = [&](int h, int ks) __attribute__((always_inline)) -> int {
@@ -343,7 +428,34 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
     const int h = t % H;
     const char* base = smem + ((t / H) % S) * C::STAGE;
     const char* bb = base + C::A_BYTES;
-    if constexpr (A8) {
+    if constexpr (C::W4) {
+      // MX operands follow the matrix unit's own K order, so that its two
+      // 32-element scale blocks of sub-step h are the tile's blocks 2h, 2h + 1:
+      // lane group q takes fp8 K elements [16 q, +16) and [32 + 16 q, +16) of
+      // the sub-step (chunks 4h + q, 4h + 2 + q) and fp4 elements [32 q, +32)
+      // (16 bytes: chunk 2h + q of the weight row), and the scales of block
+      // 2h + q of its activation row and of its weight row
+      const char* asc = bb + C::B_BYTES;
+      const char* bsc = asc + C::ASC_BYTES;
+#pragma unroll
+      for (int i = 0; i < TF; ++i) {
+        const int r = wm * TF * MF + MF * i + lr;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + r * ROWB8 + upos<ROWB8>(r, 4 * h + q) * 16);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + r * ROWB8 + upos<ROWB8>(r, 4 * h + 2 + q) * 16);
+        F.a[i] = i32x8{static_cast<int>(lo[0]), static_cast<int>(lo[1]), static_cast<int>(lo[2]),
+                       static_cast<int>(lo[3]), static_cast<int>(hi[0]), static_cast<int>(hi[1]),
+                       static_cast<int>(hi[2]), static_cast<int>(hi[3])};
+        F.sa[i] = *reinterpret_cast<const uint8_t*>(asc + 4 * r + 2 * h + q);
+      }
+#pragma unroll
+      for (int f = 0; f < WF; ++f) {
+        constexpr int RB = C::ROWBW;
+        const int tr = wrow_of(f);
+        F.b[f] = *reinterpret_cast<const u32x4*>(bb + tr * RB + upos<RB>(tr, 2 * h + q) * 16);
+        F.sb[f] = *reinterpret_cast<const uint8_t*>(bsc + 4 * tr + 2 * h + q);
+      }
+      return;
+    } else if constexpr (A8) {
       auto rd = [&](const char* tile, int row) __attribute__((always_inline)) -> i32x8 {
         const int c0 = 4 * h + 2 * q;
         const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + row * ROWB8 + upos<ROWB8>(row, c0) * 16);
@@ -385,7 +497,15 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   // Use the fragments in an empty statement so that the compiler's own wait
   // for them lands here (before the barrier) and not in front of the MFMAs.
   auto settle = [&](Frag& F) __attribute__((always_inline)) {
-    if constexpr (A8) {
+    if constexpr (C::W4) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+      for (int i = 0; i < TF; ++i) asm volatile("" ::"v"(F.a[i]), "v"(F.sa[i]));
+#pragma unroll
+      for (int f = 0; f < WF; ++f) asm volatile("" ::"v"(F.b[f]), "v"(F.sb[f]));
+#endif
+      return;
+    } else if constexpr (A8) {
       // (a 32-byte "v" operand is not valid for the host target: device pass only)
 #if defined(__HIP_DEVICE_COMPILE__)
 #pragma unroll
@@ -427,7 +547,15 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
         if (i < na) {
 #pragma unroll
           for (int f = 0; f < WF; ++f) {
-            if constexpr (A8) {
+            if constexpr (C::W4) {
+              // e2m1 weights (format code 4, the low four dwords) x e4m3
+              // activations (code 0), each with its E8M0 block scale
+              const u32x4& w = F.b[f];
+              const i32x8 w8{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
+                             static_cast<int>(w[3]), 0, 0, 0, 0};
+              acc[f][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, F.a[i], acc[f][i], 4, 0, 0,
+                                                                          F.sb[f], 0, F.sa[i]);
+            } else if constexpr (A8) {
               // e4m3 x e4m3 (format codes 0), unit block scales (exponent 127)
               acc[f][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[f], F.a[i], acc[f][i], 0, 0,
                                                                           0, 127, 0, 127);
@@ -461,11 +589,12 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
     constexpr bool OPENS = H == 1 || decltype(odd)::value;   // t + 1 opens a stage
     if constexpr (OPENS) {
       const int x = (t + 1) / H - 1;   // the stage finished by this sub-step
-      wait_newer<P, S - 2>(max(0, min(S - 2, nst - 2 - x)));
+      wait_stages(max(0, min(S - 2, nst - 2 - x)), std::integral_constant<int, S - 2>());
       settle(cur);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       readf(nxt, t + 1);   // t + 1 == nst * H reads a stale slot that is never used
+      if (x + S < nst) issue_scales(x + S);
       mma(cur, x + S < nst ? x + S : -1, I0(), IP1());
     } else {
       const int x = t / H - 1;         // its slot was freed by the last barrier
@@ -478,11 +607,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   // ---- prologue: S stages in flight, stage 0's fragments read
 #pragma unroll
   for (int st = 0; st < S; ++st)
-    if (st < nst)
+    if (st < nst) {
+      issue_scales(st);
 #pragma unroll
       for (int k = 0; k < P; ++k) issue_one(st, k);
+    }
   Frag F0, F1;
-  wait_newer<P, S - 1>(min(S - 1, nst - 1));
+  wait_stages(min(S - 1, nst - 1), std::integral_constant<int, S - 1>());
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   readf(F0, 0);
@@ -520,7 +651,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
       const int r = row0 + wm * TF * MF + i * MF + lr;
       if (r >= row1 || !col_ok) continue;
       float ra = 1.f;   // the row's activation scale (fp8 activations)
-      if constexpr (A8) ra = Sg.a_scale[Sg.gather ? Sg.gather[r] : r];
+      if constexpr (A8 && !C::W4) ra = Sg.a_scale[Sg.gather ? Sg.gather[r] : r];
       float v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -554,6 +685,15 @@ hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, int 
   using CB = Cfg<BM, BNW, WM, WN, BPC, false, 32, MF>;
   // fp8 weights 64 deep where three such stages fit in the block's LDS share
   using C8 = Cfg<BM, BNW, WM, WN, BPC, true, (BPC == 1 ? 64 : 32), MF>;
+  if (a_dtype == DT_MXFP8) {
+    // MXFP8 x MXFP4: one block per CU, scaled 32x32x64 MFMAs, 128-deep stages
+    if constexpr (BPC == 1) {
+      using CW = Cfg<BM, BNW, WM, WN, 1, true, 128, 32, true, true>;
+      if (w_dtype != DT_MXFP4 || out_dtype != DT_BF16) return hipErrorInvalidValue;
+      return gated ? launch_one<CW, true, DT_MXFP4, DT_BF16>(g, s) : launch_one<CW, false, DT_MXFP4, DT_BF16>(g, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (a_dtype == DT_FP8) {
     // fp8 x fp8: one block per CU, 32x32x64 MFMAs
     if constexpr (BPC == 1) {
@@ -592,8 +732,8 @@ int tiled_blocks_n(int shape, bool gated, int n_out) {
 }
 
 bool tiled_offsets_fit(int64_t a_rows, int64_t lda, int64_t w_rows, int64_t K, int w_dtype) {
-  const int64_t wb = w_dtype == DT_FP8 ? 1 : 2;
-  return a_rows * lda * 2 < (int64_t(1) << 32) && w_rows * K * wb < (int64_t(1) << 32);
+  const int64_t w_bytes = w_dtype == DT_MXFP4 ? w_rows * K / 2 : w_rows * K * (w_dtype == DT_FP8 ? 1 : 2);
+  return a_rows * lda * 2 < (int64_t(1) << 32) && w_bytes < (int64_t(1) << 32);
 }
 
 hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype, int out_dtype,
@@ -604,6 +744,9 @@ hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype,
     const int ks = S.ksplit > 1 ? S.ksplit : 1;
     if ((S.K / ks) % (2 * KS) || S.bm != tiled_bm(shape) || S.n_out % 4) return hipErrorInvalidValue;
     if (a_dtype == DT_FP8 && ((S.K / ks) % tiled_k_multiple_a8() || !S.a_scale)) return hipErrorInvalidValue;
+    if (a_dtype == DT_MXFP8 && ((S.K / ks) % tiled_k_multiple_a8() || !S.a_mx || !S.w_mx ||
+                                S.a_mx_rows < S.a_rows || S.NB % 4))
+      return hipErrorInvalidValue;
     if (!tiled_offsets_fit(S.a_rows, S.lda, S.NB, S.K, w_dtype)) return hipErrorInvalidValue;
   }
   switch (shape) {

@@ -7,7 +7,9 @@
 namespace moe {
 
 // ------------------------------------------------------------------ dtypes
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+// DT_MXFP4: e2m1 pairs per byte (element 2j in the low nibble) with E8M0
+// block scales; DT_MXFP8: e4m3fn codes with E8M0 block scales (activations)
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3, DT_MXFP8 = 4 };
 enum : int { ACT_SILU = 0, ACT_GELU_TANH = 1 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -42,6 +44,13 @@ struct GSet {
   const int32_t* gather;    // A row of set row r = gather ? gather[r] : r
   int64_t lda;
   const float* a_scale;     // fp8 A: per-A-row (storage row) dequantisation scale
+  // MX block scales (E8M0 bytes; per group of 128 K elements, a row's four
+  // block scales side by side): A rows [K/128][a_mx_rows][4] (storage rows),
+  // weights [groups][K/128][NB][4]
+  const uint8_t* a_mx;
+  int32_t a_mx_rows;
+  const uint8_t* w_mx;
+  int64_t w_mx_gstride;     // bytes between groups' weight scales
   const void* w;            // [groups][NB][K] weight storage
   const float* scale;       // [groups][NB] per-output-channel scales or null
   int64_t w_gstride;        // elements between groups (NB*K)
@@ -176,7 +185,9 @@ int stream_max_mt(int a_dtype);              // largest mt the stream kernel run
 // must be tiled_bm(shape).
 enum : int { TILED_TALL = 0, TILED_WIDE = 1, TILED_NARROW = 2 };
 // a_dtype DT_FP8 (fp8 activations with fp8 weights, bf16 output, one block
-// per CU shapes only) needs every set's a_scale.
+// per CU shapes only) needs every set's a_scale; a_dtype DT_MXFP8 (with
+// DT_MXFP4 weights, same shapes and output) every set's a_mx and w_mx, with
+// a_mx_rows >= a_rows.
 hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype, int out_dtype,
                              int a_dtype, hipStream_t s);
 int tiled_bm(int shape);
@@ -192,6 +203,14 @@ bool tiled_offsets_fit(int64_t a_rows, int64_t lda, int64_t w_rows, int64_t K, i
 int quant_max_cols();
 hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q,
                              float* scale, hipStream_t s);
+// MXFP8 quantisation of bf16 rows: per block of 32 elements an E8M0 scale
+// 2^(floor(log2 amax) - 8) (clamped to [2^-127, 2^127]; 2^-127 for a zero
+// block) and e4m3fn codes of a / scale (nearest even, saturating).  Scales go
+// to scale[(c / 128) * rows + r][(c % 128) / 32] (rows side by side per group of
+// 128 columns).
+// cols % 128 == 0, cols <= quant_max_cols().
+hipError_t launch_quant_rows_mx(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q,
+                                uint8_t* scale, hipStream_t s);
 
 // Decode n (multiple of 8) fp8 e4m3fn codes to bf16 with the GEMM's own decoder.
 hipError_t launch_fp8_decode(const uint8_t* codes, uint16_t* out, int n, hipStream_t s);

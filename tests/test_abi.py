@@ -66,6 +66,8 @@ def _ok_problem(**over):
     (dict(w_dtype=B.MOE_BF16), B.MOE_ERR_UNSUPPORTED),              # f32 act x bf16 weights
     (dict(act_dtype=B.MOE_FP8_E4M3FN), B.MOE_ERR_UNSUPPORTED),
     (dict(renormalize=2), B.MOE_ERR_UNSUPPORTED), (dict(act_quant=2), B.MOE_ERR_UNSUPPORTED),
+    (dict(act_quant=3), B.MOE_ERR_UNSUPPORTED), (dict(act_quant=-1), B.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=B.MOE_MXFP4_E2M1), B.MOE_ERR_DTYPE),               # weights-only format
     (dict(act_quant=1), B.MOE_ERR_UNSUPPORTED),                       # fp32 layer: no fp8 path
     (dict(renormalize=0), B.MOE_OK),
 ])
@@ -98,6 +100,58 @@ def test_act_quant_validation(lib, over, status):
     if status == B.MOE_OK:
         p0 = _fp8_problem(act_quant=0, **over)
         assert n.value > B.moe_layer_workspace_size(p0)    # fp8 copies of x and h live there
+
+
+def _mx_problem(**over):
+    p = B.make_problem(64, 256, 8, 2, 128, 128, act_dtype="bf16", w_dtype="mxfp4",
+                       act_quant=B.MOE_ACT_QUANT_MXFP8)
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(), B.MOE_OK), (dict(I_shared=0), B.MOE_OK),
+    (dict(act_quant=B.MOE_ACT_QUANT_NONE), B.MOE_ERR_UNSUPPORTED),     # MXFP4 needs MXFP8 activations
+    (dict(act_quant=B.MOE_ACT_QUANT_FP8_ROW), B.MOE_ERR_UNSUPPORTED),
+    (dict(w_dtype=B.MOE_FP8_E4M3FN), B.MOE_ERR_UNSUPPORTED),            # MXFP8 needs MXFP4 weights
+    (dict(shared_w_dtype=B.MOE_FP8_E4M3FN), B.MOE_ERR_UNSUPPORTED),
+    (dict(shared_w_dtype=B.MOE_BF16, I_shared=0), B.MOE_OK),            # no shared branch: unused
+    (dict(tile_policy=B.MOE_TILE_STREAM), B.MOE_ERR_UNSUPPORTED),
+    (dict(D=192), B.MOE_ERR_UNSUPPORTED), (dict(I=64), B.MOE_ERR_UNSUPPORTED),
+    (dict(I_shared=64), B.MOE_ERR_UNSUPPORTED), (dict(D=32768), B.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=B.MOE_F32), B.MOE_ERR_UNSUPPORTED),
+])
+def test_mx_validation(lib, over, status):
+    p = _mx_problem(**over)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_layer_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+    assert lib.moe_grouped_ffn_workspace_size(ctypes.byref(p), 8, 128, ctypes.byref(n)) == status
+
+
+def test_mx_workspace_holds_the_block_scales(lib):
+    """The MXFP8 copies of x, h and h_shared take one byte per element plus
+    one scale byte per 32 elements."""
+    p, p0 = _mx_problem(T=1000), _mx_problem(T=1000)
+    p0.act_quant, p0.w_dtype, p0.shared_w_dtype = 0, B.MOE_BF16, B.MOE_BF16
+    T, D, k, I, Is = 1000, 256, 2, 128, 128
+    extra = B.moe_layer_workspace_size(p) - B.moe_layer_workspace_size(p0)
+    want = (T * D + T * k * I + T * Is) * (1 + 1 / 32)
+    assert want <= extra <= want + 6 * 256
+
+
+def test_quantize_rows_mx_validation(lib):
+    fake = 4096
+    f = lib.moe_quantize_rows_mx
+    assert f(fake, 4, 64, 64, fake, fake, None) == B.MOE_ERR_SHAPE        # cols % 128
+    assert f(fake, 4, 256, 128, fake, fake, None) == B.MOE_ERR_SHAPE      # lda < cols
+    assert f(fake, 4, 128, 132, fake, fake, None) == B.MOE_ERR_SHAPE      # lda % 8
+    assert f(fake, 4, 1 << 15, 1 << 15, fake, fake, None) == B.MOE_ERR_SHAPE
+    assert f(fake, -1, 128, 128, fake, fake, None) == B.MOE_ERR_SHAPE
+    assert f(fake + 8, 4, 128, 128, fake, fake, None) == B.MOE_ERR_SHAPE   # a 16-byte aligned
+    assert f(None, 4, 128, 128, fake, fake, None) == B.MOE_ERR_NULL
+    assert f(fake, 4, 128, 128, fake, None, None) == B.MOE_ERR_NULL
+    assert f(None, 0, 128, 128, None, None, None) == B.MOE_OK
 
 
 def test_quantize_rows_validation(lib):
