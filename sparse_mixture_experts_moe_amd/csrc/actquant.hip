@@ -9,6 +9,12 @@
 // of zeros), each element becomes the e4m3fn code nearest to a / scale (ties
 // to the even code, saturating at +-448), with both divisions correctly
 // rounded in fp32.
+//
+// The MXFP8 variant is the activation side of the W4A8 decomposition ("CANN
+// Qwen3-MoE" page, high-throughput prefill), with the OCP microscaling block
+// format: per 32 elements an E8M0 scale 2^(floor(log2 amax) - 8), clamped to
+// exponents [-127, 127], and e4m3fn codes of a / scale; the scaling is an
+// exact power of two, so only the code rounding (nearest even) is inexact.
 #include "moe_kernels.h"
 
 namespace moe {

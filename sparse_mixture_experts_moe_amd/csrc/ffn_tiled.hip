@@ -43,6 +43,13 @@
 // bf16 rate), stages are 128 deep (128-byte requests for both operands) and
 // the epilogue multiplies by the row's activation scale as well.
 //
+// W4A8 ("CANN Qwen3-MoE" page, high-throughput prefill: MXFP4 weights, MXFP8
+// activations): the weight tile holds e2m1 pairs, and each stage also stages
+// the E8M0 block scales of its activation rows and weight rows (4 bytes per
+// row per 128-deep stage), which the scaled MFMA applies per 32-element block.
+// Fragments follow the matrix unit's own K order so that each of its two
+// scale blocks per MFMA is exactly one MX block.
+//
 // A tile row of RB bytes holds RB / 16 chunks of 16 bytes; chunk c of row r
 // sits at a position XORed with a few bits of r (upos below), chosen so that
 // the rows sharing a 256-byte line of the 64 banks, and the rows one fragment
