@@ -639,7 +639,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   // each group's scales are loaded once.
   const float* sc = Sg.scale ? Sg.scale + group * Sg.s_gstride : nullptr;
   constexpr int OCOLS = GATED ? BNW / 2 / C::WN : BNW / C::WN;   // output columns per wavefront
-  constexpr int NG = MF / 8;                                     // column groups per fragment and lane
+  constexpr int NG = MF == 16 ? 1 : MF / 8;                      // column groups per fragment and lane
   const int col_w = n0 + wn * OCOLS;
   char* outb = static_cast<char*>(Sg.out) + split * Sg.split_stride * (ODT == DT_F32 ? 4 : 2);
 #pragma unroll
