@@ -139,6 +139,17 @@ constexpr bool kTiledReady = true;
 #ifndef MOE_TALL_MEAN
 #define MOE_TALL_MEAN 192.0
 #endif
+// fp8 weights: groups averaging more than MOE_SMALL_MIN and at most
+// MOE_SMALL_MAX rows run on the tiled GEMM's 32-row shape (0 = off).
+#ifndef MOE_TILED_SMALL
+#define MOE_TILED_SMALL 1
+#endif
+#ifndef MOE_SMALL_MIN
+#define MOE_SMALL_MIN 8.0
+#endif
+#ifndef MOE_SMALL_MAX
+#define MOE_SMALL_MAX 48.0
+#endif
 
 
 // The tiled GEMM's 32-bit offsets cover every operand of the expert FFNs.
@@ -159,6 +170,10 @@ Plan make_plan(const moe_problem_t* p, double mean_rows) {
   }
   const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16 && tiled_fits(p);
   int policy = p->tile_policy;
+  if (MOE_TILED_SMALL && policy == MOE_TILE_AUTO && tiled_ok && p->w_dtype == MOE_FP8_E4M3FN &&
+      (!p->I_shared || p->shared_w_dtype == MOE_FP8_E4M3FN) && mean_rows > MOE_SMALL_MIN &&
+      mean_rows <= MOE_SMALL_MAX)
+    return Plan{true, 0, tiled_bm(TILED_SMALL), TILED_SMALL};
   if (policy == MOE_TILE_AUTO) policy = (tiled_ok && mean_rows > 48.0) ? MOE_TILE_LDS : MOE_TILE_STREAM;
   if (policy == MOE_TILE_LDS && tiled_ok) {
     // 256-row tiles read an expert's weights half as often; measured faster

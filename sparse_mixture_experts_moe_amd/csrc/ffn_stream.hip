@@ -33,13 +33,13 @@ namespace moe {
 namespace {
 
 // 16-row weight fragments per wavefront (build-time tuning knob MOE_STREAM_NF:
-// 4 or 2); a gated wavefront holds NF/2 gate and NF/2 up fragments
+// 2, 4 or 8); a gated wavefront holds NF/2 gate and NF/2 up fragments
 #ifndef MOE_STREAM_NF
 #define MOE_STREAM_NF 4
 #endif
 constexpr int NF = MOE_STREAM_NF;
 constexpr int WROWS = 16 * NF;   // weight rows per wavefront
-static_assert(NF == 2 || NF == 4, "fragments per wavefront");
+static_assert(NF == 2 || NF == 4 || NF == 8, "fragments per wavefront");
 constexpr int WAVES = 4;         // wavefronts per block (consecutive N tiles)
 
 // Build-time tuning knobs (defaults are the measured choice):
@@ -54,6 +54,10 @@ constexpr int WAVES = 4;         // wavefronts per block (consecutive N tiles)
 //   MOE_STREAM_U2  K-steps per register stage when tiles are two 16-row chunks
 #ifndef MOE_STREAM_U2
 #define MOE_STREAM_U2 4
+#endif
+//   MOE_STREAM_AGPR  1: accumulators in AGPRs
+#ifndef MOE_STREAM_AGPR
+#define MOE_STREAM_AGPR 0
 #endif
 
 __device__ __forceinline__ uint4 load_w(const uint4* p) {
@@ -81,6 +85,11 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
   constexpr int AV = VecCount<ADT, U>::n;   // uint4 per lane per stage, A
   constexpr int BV = VecCount<WDT, U>::n;   // uint4 per lane per stage, B (per fragment)
   constexpr int KS = 32 * U;                // K elements per stage
+#if MOE_STREAM_AGPR
+  // an (empty) statement naming an accumulation register: the MFMAs then use
+  // the AGPR form and the accumulators leave the VGPRs to the register stages
+  asm volatile("" ::: "a0");
+#endif
   int si, group, row0, row1, nblk;
   if (!resolve_block(g, blockIdx.x, si, group, row0, row1, nblk)) return;
   const GSet& S = g.s[si];

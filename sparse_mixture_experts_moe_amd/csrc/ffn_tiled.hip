@@ -133,8 +133,10 @@ template <int RB> __device__ __forceinline__ int upos(int row, int c) {
 // sbase and lds are wave-uniform.  Issued through inline asm so the compiler
 // does not conservatively wait for every copy in flight before each LDS read;
 // completion is tracked explicitly with wait_vm below.
+// NT: the streaming (non-temporal) cache hint, for data read exactly once.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT = false>
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, const void* lds) {
   const uint32_t l = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds))));
@@ -142,8 +144,12 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, const vo
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
   const uint64_t bs = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bs), "s"(l)
-               : "memory", "m0");
+  if constexpr (NT)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(bs), "s"(l)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bs), "s"(l)
+                 : "memory", "m0");
 }
 // Same with 4 bytes per lane (to lds + 4 * lane).
 __device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, const void* lds) {
@@ -187,9 +193,19 @@ template <int P, int M> __device__ __forceinline__ void wait_newer(int newer) {
 #ifndef MOE_TILED_REMAP
 #define MOE_TILED_REMAP 0
 #endif
+// Same for the 32-row shape only.
+#ifndef MOE_SMALL_REMAP
+#define MOE_SMALL_REMAP 0
+#endif
+// 32-row shape: weight copies carry the streaming hint (each weight byte is
+// read once per launch; the activation rows are re-read by every N block)
+#ifndef MOE_SMALL_NT
+#define MOE_SMALL_NT 0
+#endif
 constexpr int NXCD = 8;   // XCDs; workgroup i is dispatched to XCD i % NXCD
+template <class C> constexpr bool remapped() { return MOE_TILED_REMAP || (MOE_SMALL_REMAP && C::BM == 32); }
 
-#if MOE_TILED_REMAP
+#if MOE_TILED_REMAP || MOE_SMALL_REMAP
 // Logical block of a physical one.  Workgroups are dispatched round-robin over
 // the XCDs, so XCD x runs blocks x, x + 8, x + 16, ...; the remap gives each
 // XCD one contiguous, equal share of the blocks that exist (the M-tiles of a
@@ -236,8 +252,9 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   // the VGPRs stay free for fragments.
   asm volatile("" ::: "a0");
   int b = blockIdx.x;
-#if MOE_TILED_REMAP
-  if (!remap_block(g, b)) return;
+#if MOE_TILED_REMAP || MOE_SMALL_REMAP
+  if constexpr (remapped<C>())
+    if (!remap_block(g, b)) return;
 #endif
   int si, group, row0, row1, nblk;
   if (!resolve_block(g, b, si, group, row0, row1, nblk)) return;
@@ -327,8 +344,8 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
       dma16(a_off[k], a_base + st * ROWA, base + (wave * C::AL + k) * 1024);
     } else {
       const int i = k - C::AL;
-      dma16(b_off[i], b_base + st * C::ROWBW,
-            base + C::A_BYTES + (wave * C::BL + i) * 1024);
+      dma16<C::BM == 32 && MOE_SMALL_NT>(b_off[i], b_base + st * C::ROWBW,
+                                         base + C::A_BYTES + (wave * C::BL + i) * 1024);
     }
   };
   // MX block scales: wavefront w < NSC copies one part of stage st's scales --
@@ -682,7 +699,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
 
 template <class C, bool GATED, int WDT, int ODT>
 hipError_t launch_one(const GArgs& g, hipStream_t s) {
-  const int grid = MOE_TILED_REMAP ? (g.total_blocks + NXCD - 1) / NXCD * NXCD : g.total_blocks;
+  const int grid = remapped<C>() ? (g.total_blocks + NXCD - 1) / NXCD * NXCD : g.total_blocks;
   tiled_gemm_kernel<C, GATED, WDT, ODT><<<grid, C::THREADS, 0, s>>>(g);
   return hipGetLastError();
 }
@@ -721,12 +738,31 @@ hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, int 
   return hipErrorInvalidValue;
 }
 
+// Decode-sized groups with fp8 weights: 32 rows x 256 weight rows, four
+// wavefronts of 32 rows x 64 weight rows, two blocks per CU, 64-deep stages in
+// a ring of four.  Streaming the weights through the LDS ring keeps three
+// stages (about 120 KiB per CU) in flight without holding them in registers.
+#ifndef MOE_SMALL_BNW
+#define MOE_SMALL_BNW 256     // build-time knobs: block width and blocks per CU
+#endif
+#ifndef MOE_SMALL_BPC
+#define MOE_SMALL_BPC (MOE_SMALL_BNW == 256 ? 2 : 1)
+#endif
+hipError_t dispatch_small(const GArgs& g, bool gated, int w_dtype, int out_dtype, int a_dtype,
+                          hipStream_t s) {
+  using C = Cfg<32, MOE_SMALL_BNW, 1, 4, MOE_SMALL_BPC, true, 64, 16>;
+  if (a_dtype != DT_BF16 || w_dtype != DT_FP8 || out_dtype != DT_BF16) return hipErrorInvalidValue;
+  return gated ? launch_one<C, true, DT_FP8, DT_BF16>(g, s) : launch_one<C, false, DT_FP8, DT_BF16>(g, s);
+}
+
 // weight rows per block of a shape
-int block_width(int shape) { return shape == TILED_WIDE ? 512 : 256; }
+int block_width(int shape) {
+  return shape == TILED_WIDE ? 512 : shape == TILED_SMALL ? MOE_SMALL_BNW : 256;
+}
 
 }  // namespace
 
-int tiled_bm(int shape) { return shape == TILED_TALL ? 256 : 128; }
+int tiled_bm(int shape) { return shape == TILED_TALL ? 256 : shape == TILED_SMALL ? 32 : 128; }
 
 int tiled_k_multiple() { return 2 * KS; }
 
@@ -760,6 +796,7 @@ hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype,
     case TILED_TALL: return dispatch<256, 256, 4, 2, 1, 16>(g, gated, w_dtype, out_dtype, a_dtype, s);
     case TILED_WIDE: return dispatch<128, 512, 2, 4, 1, 16>(g, gated, w_dtype, out_dtype, a_dtype, s);
     case TILED_NARROW: return dispatch<128, 256, 2, 2, 2, 16>(g, gated, w_dtype, out_dtype, a_dtype, s);
+    case TILED_SMALL: return dispatch_small(g, gated, w_dtype, out_dtype, a_dtype, s);
   }
   return hipErrorInvalidValue;
 }

@@ -26,6 +26,10 @@ SMALL = {
     "big_groups_bf16": shrink(CONFIGS["qwen_prefill"], T=1100, D=256, E=4, k=2, I=192, I_shared=128,
                               zipf=False),
     "big_groups_fp8": shrink(CONFIGS["ling_prefill"], T=1030, D=320, E=4, k=2, I=128, I_shared=192),
+    # fp8 weights, about 12 rows per expert with Zipf-skewed loads (empty experts
+    # and experts over 32 rows): the automatic policy's 32-row tiled shape
+    "ling_decode_like": shrink(CONFIGS["ling_decode"], T=200, D=512, E=64, k=4, I=256, I_shared=256,
+                               zipf=True),
 }
 
 
@@ -56,7 +60,7 @@ def test_fp8_decode_all_256_codes():
 
 
 # ------------------------------------------------------------------ whole layer, small
-@pytest.mark.parametrize("policy", ["stream", "lds"])
+@pytest.mark.parametrize("policy", ["stream", "lds", "auto"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_layer_small_with_oracle_logits(name, policy):
     cfg = SMALL[name]
@@ -246,8 +250,8 @@ def test_moe_combine_reproduces_gathered_rows():
     assert rel_err(y.cpu().numpy(), x.numpy()) < 1e-6
 
 
-@pytest.mark.parametrize("policy", ["stream", "lds"])
-@pytest.mark.parametrize("name", ["qwen_ragged", "ling_fp8", "gemma_like"])
+@pytest.mark.parametrize("policy", ["stream", "lds", "auto"])
+@pytest.mark.parametrize("name", ["qwen_ragged", "ling_fp8", "gemma_like", "ling_decode_like"])
 def test_moe_grouped_ffn_entry(name, policy):
     """Grouped FFN alone on permuted rows, and the shared branch as one group."""
     cfg = SMALL[name]
