@@ -170,9 +170,10 @@ Plan make_plan(const moe_problem_t* p, double mean_rows) {
   }
   const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16 && tiled_fits(p);
   int policy = p->tile_policy;
+  const int ks = tiled_k_multiple_small();
   if (MOE_TILED_SMALL && policy == MOE_TILE_AUTO && tiled_ok && p->w_dtype == MOE_FP8_E4M3FN &&
       (!p->I_shared || p->shared_w_dtype == MOE_FP8_E4M3FN) && mean_rows > MOE_SMALL_MIN &&
-      mean_rows <= MOE_SMALL_MAX)
+      mean_rows <= MOE_SMALL_MAX && p->D % ks == 0 && p->I % ks == 0 && p->I_shared % ks == 0)
     return Plan{true, 0, tiled_bm(TILED_SMALL), TILED_SMALL};
   if (policy == MOE_TILE_AUTO) policy = (tiled_ok && mean_rows > 48.0) ? MOE_TILE_LDS : MOE_TILE_STREAM;
   if (policy == MOE_TILE_LDS && tiled_ok) {

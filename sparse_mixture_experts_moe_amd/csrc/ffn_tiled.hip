@@ -110,10 +110,10 @@ struct Cfg {
   static constexpr int AL = A_BYTES / 1024 / NW;      // 1 KiB copy instructions per wavefront, A
   static constexpr int BL = B_BYTES / 1024 / NW;      // same, B
   static constexpr int P = AL + BL;
-  static constexpr int P1 = (P + H - 1) / H;          // copies issued in a stage's first sub-step
+  static constexpr int P1 = (P + H - 1) / H;          // copies issued per sub-step (the last chunk fewer)
   static_assert(AL * NW * 1024 == A_BYTES && BL * NW * 1024 == B_BYTES, "copy split");
-  static_assert(H == 1 || H == 2, "stage depth");
-  static_assert(S >= 3 || (S == 2 && H == 2), "ring depth");
+  static_assert(H == 1 || H == 2 || H == 4, "stage depth");
+  static_assert(S >= 3 || (S == 2 && H >= 2), "ring depth");
   static_assert(TF * WF * MF * MF / 64 * WPE <= 256, "accumulators fit the AGPRs");
   static_assert(WPE == 1 || WPE == 2, "one or two wavefronts per SIMD");
   static_assert(!A8 || (FP8 && MF == 32), "fp8 activations: fp8 weights, 32x32x64 MFMAs");
@@ -125,7 +125,7 @@ struct Cfg {
 // 256 / RB rows share a line of the 64 banks, and consecutive groups of them
 // XOR the chunk index with consecutive values
 template <int RB> __device__ __forceinline__ int upos(int row, int c) {
-  constexpr int SH = RB == 32 ? 3 : RB == 64 ? 2 : 1;
+  constexpr int SH = RB == 32 ? 3 : RB == 64 ? 2 : RB == 128 ? 1 : 0;
   return c ^ ((row >> SH) & (RB / 16 - 1));
 }
 
@@ -601,17 +601,19 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
       }
     }
   };
-  using I0 = std::integral_constant<int, 0>;
-  using IP1 = std::integral_constant<int, C::P1>;
-  using IP = std::integral_constant<int, P>;
-  // Sub-step t.  When sub-step t + 1 opens a stage, that stage has landed
-  // (own copies; everyone's after the barrier, which also frees the slot of
-  // the stage just finished for the stage S further on, whose copies go out
-  // during this sub-step and, with two sub-steps per stage, the next one).
+  // copies [c P1, (c + 1) P1) of a stage: chunk c of its H chunks
+  constexpr int P1 = C::P1;
+  auto chunk_lo = [](auto c) { return std::integral_constant<int, (decltype(c)::value * P1 < P ? decltype(c)::value * P1 : P)>(); };
+  auto chunk_hi = [](auto c) { return std::integral_constant<int, ((decltype(c)::value + 1) * P1 < P ? (decltype(c)::value + 1) * P1 : P)>(); };
+  // Sub-step t, phase PH = t % H within its stage.  When sub-step t + 1 opens
+  // a stage (PH == H - 1), that stage has landed (own copies; everyone's after
+  // the barrier, which also frees the slot of the stage just finished for the
+  // stage S further on).  That stage's copies go out in H chunks: the first
+  // in this sub-step, the others in the next stage's first H - 1 sub-steps.
   // Sub-step t + 1's fragments are read while t's MFMAs run.
-  auto step = [&](Frag& cur, Frag& nxt, int t, auto odd) __attribute__((always_inline)) {
-    constexpr bool OPENS = H == 1 || decltype(odd)::value;   // t + 1 opens a stage
-    if constexpr (OPENS) {
+  auto step = [&](Frag& cur, Frag& nxt, int t, auto ph) __attribute__((always_inline)) {
+    constexpr int PH = decltype(ph)::value;
+    if constexpr (PH == H - 1) {
       const int x = (t + 1) / H - 1;   // the stage finished by this sub-step
       wait_stages(max(0, min(S - 2, nst - 2 - x)), std::integral_constant<int, S - 2>());
       settle(cur);
@@ -619,12 +621,14 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
       asm volatile("" ::: "memory");
       readf(nxt, t + 1);   // t + 1 == nst * H reads a stale slot that is never used
       if (x + S < nst) issue_scales(x + S);
-      mma(cur, x + S < nst ? x + S : -1, I0(), IP1());
+      using c0 = std::integral_constant<int, 0>;
+      mma(cur, x + S < nst ? x + S : -1, chunk_lo(c0()), chunk_hi(c0()));
     } else {
       const int x = t / H - 1;         // its slot was freed by the last barrier
       settle(cur);                     // (decodes fp8 weights)
       readf(nxt, t + 1);
-      mma(cur, x >= 0 && x + S < nst ? x + S : -1, IP1(), IP());
+      using cc = std::integral_constant<int, PH + 1>;
+      mma(cur, x >= 0 && x + S < nst ? x + S : -1, chunk_lo(cc()), chunk_hi(cc()));
     }
   };
 
@@ -641,11 +645,24 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   readf(F0, 0);
-  // nst * H sub-steps, an even number (with one sub-step per stage, nst is
-  // even: checked by the launcher)
-  for (int t = 0; t < nst * H; t += 2) {
-    step(F0, F1, t, std::false_type());
-    step(F1, F0, t + 1, std::true_type());
+  // nst * H sub-steps, a multiple of 2 and of H (with one sub-step per stage,
+  // nst is even: checked by the launcher)
+  using Ph0 = std::integral_constant<int, 0>;
+  using Ph1 = std::integral_constant<int, 1 % H>;
+  using Ph2 = std::integral_constant<int, 2 % H>;
+  using Ph3 = std::integral_constant<int, 3 % H>;
+  if constexpr (H == 4) {
+    for (int t = 0; t < nst * H; t += 4) {
+      step(F0, F1, t, Ph0());
+      step(F1, F0, t + 1, Ph1());
+      step(F0, F1, t + 2, Ph2());
+      step(F1, F0, t + 3, Ph3());
+    }
+  } else {
+    for (int t = 0; t < nst * H; t += 2) {
+      step(F0, F1, t, Ph0());
+      step(F1, F0, t + 1, Ph1());
+    }
   }
   wait_vm<0>();   // no copy may still be in flight when the block retires
 
@@ -739,18 +756,24 @@ hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, int 
 }
 
 // Decode-sized groups with fp8 weights: 32 rows x 256 weight rows, four
-// wavefronts of 32 rows x 64 weight rows, two blocks per CU, 64-deep stages in
-// a ring of four.  Streaming the weights through the LDS ring keeps three
-// stages (about 120 KiB per CU) in flight without holding them in registers.
+// wavefronts of 32 rows x 64 weight rows, two blocks per CU, 128-deep stages
+// (128-byte weight-row requests, four MFMA sub-steps per stage) in a ring of
+// two.  Streaming the weights through the LDS ring keeps a stage per block in
+// flight without holding it in registers.
 #ifndef MOE_SMALL_BNW
-#define MOE_SMALL_BNW 256     // build-time knobs: block width and blocks per CU
+#define MOE_SMALL_BNW 128     // build-time knobs: block width and blocks per CU
 #endif
 #ifndef MOE_SMALL_BPC
-#define MOE_SMALL_BPC (MOE_SMALL_BNW == 256 ? 2 : 1)
+#define MOE_SMALL_BPC (MOE_SMALL_BNW <= 256 ? 2 : 1)
+#endif
+#ifndef MOE_SMALL_BK
+#define MOE_SMALL_BK 128
 #endif
 hipError_t dispatch_small(const GArgs& g, bool gated, int w_dtype, int out_dtype, int a_dtype,
                           hipStream_t s) {
-  using C = Cfg<32, MOE_SMALL_BNW, 1, 4, MOE_SMALL_BPC, true, 64, 16>;
+  using C = Cfg<32, MOE_SMALL_BNW, 1, 4, MOE_SMALL_BPC, true, MOE_SMALL_BK, 16>;
+  for (int i = 0; i < g.nsets; ++i)
+    if ((g.s[i].K / (g.s[i].ksplit > 1 ? g.s[i].ksplit : 1)) % C::BK) return hipErrorInvalidValue;
   if (a_dtype != DT_BF16 || w_dtype != DT_FP8 || out_dtype != DT_BF16) return hipErrorInvalidValue;
   return gated ? launch_one<C, true, DT_FP8, DT_BF16>(g, s) : launch_one<C, false, DT_FP8, DT_BF16>(g, s);
 }
@@ -768,6 +791,8 @@ int tiled_k_multiple() { return 2 * KS; }
 
 // fp8 x fp8: K a multiple of the 128-deep stage (or of two 64-deep ones)
 int tiled_k_multiple_a8() { return 128; }
+
+int tiled_k_multiple_small() { return MOE_SMALL_BK; }
 
 int tiled_blocks_n(int shape, bool gated, int n_out) {
   const int w = gated ? block_width(shape) / 2 : block_width(shape);

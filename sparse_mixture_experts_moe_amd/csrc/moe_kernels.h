@@ -194,6 +194,7 @@ hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype,
 int tiled_bm(int shape);
 int tiled_k_multiple();                      // every K (slice) must be a multiple of this
 int tiled_k_multiple_a8();                   // the same with fp8 activations
+int tiled_k_multiple_small();                // the same for TILED_SMALL
 int tiled_blocks_n(int shape, bool gated, int n_out);
 // The tiled GEMM addresses A rows and one group's weights with 32-bit byte offsets.
 bool tiled_offsets_fit(int64_t a_rows, int64_t lda, int64_t w_rows, int64_t K, int w_dtype);
