@@ -150,6 +150,10 @@ constexpr bool kTiledReady = true;
 #ifndef MOE_SMALL_MAX
 #define MOE_SMALL_MAX 48.0
 #endif
+// bf16 weights on the 32-row shape too, below MOE_SMALL_MAX rows per group
+#ifndef MOE_SMALL_BF16
+#define MOE_SMALL_BF16 1
+#endif
 
 
 // The tiled GEMM's 32-bit offsets cover every operand of the expert FFNs.
@@ -171,9 +175,13 @@ Plan make_plan(const moe_problem_t* p, double mean_rows) {
   const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16 && tiled_fits(p);
   int policy = p->tile_policy;
   const int ks = tiled_k_multiple_small();
-  if (MOE_TILED_SMALL && policy == MOE_TILE_AUTO && tiled_ok && p->w_dtype == MOE_FP8_E4M3FN &&
-      (!p->I_shared || p->shared_w_dtype == MOE_FP8_E4M3FN) && mean_rows > MOE_SMALL_MIN &&
-      mean_rows <= MOE_SMALL_MAX && p->D % ks == 0 && p->I % ks == 0 && p->I_shared % ks == 0)
+  const bool small_bf16 = MOE_SMALL_BF16 && p->w_dtype == MOE_BF16 &&
+                          (!p->I_shared || p->shared_w_dtype == MOE_BF16) && mean_rows <= MOE_SMALL_MAX;
+  const bool small_fp8 = p->w_dtype == MOE_FP8_E4M3FN &&
+                         (!p->I_shared || p->shared_w_dtype == MOE_FP8_E4M3FN) &&
+                         mean_rows > MOE_SMALL_MIN && mean_rows <= MOE_SMALL_MAX;
+  if (MOE_TILED_SMALL && policy == MOE_TILE_AUTO && tiled_ok && (small_fp8 || small_bf16) &&
+      p->D % ks == 0 && p->I % ks == 0 && p->I_shared % ks == 0)
     return Plan{true, 0, tiled_bm(TILED_SMALL), TILED_SMALL};
   if (policy == MOE_TILE_AUTO) policy = (tiled_ok && mean_rows > 48.0) ? MOE_TILE_LDS : MOE_TILE_STREAM;
   if (policy == MOE_TILE_LDS && tiled_ok) {
@@ -670,7 +678,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
                                    idx, tw, s));
   }
   // 2. permutation and the M-tile table (one launch for small batches)
-  if (p->T <= perm_small_max_tokens() && !pl.tiled) {
+  if (p->T <= perm_small_max_tokens() && (!pl.tiled || pl.shape == TILED_SMALL)) {
     StageScope sc(ST_PERMUTE, s);
     MOE_LAUNCH(launch_permute_small(idx, p->T, p->k, p->E, counts, offsets, row_token, row_of_slot,
                                     pl.bm, L.tile_ub, tiles, ntiles, s));

@@ -755,11 +755,11 @@ hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, int 
   return hipErrorInvalidValue;
 }
 
-// Decode-sized groups with fp8 weights: 32 rows x 256 weight rows, four
-// wavefronts of 32 rows x 64 weight rows, two blocks per CU, 128-deep stages
-// (128-byte weight-row requests, four MFMA sub-steps per stage) in a ring of
-// two.  Streaming the weights through the LDS ring keeps a stage per block in
-// flight without holding it in registers.
+// Decode-sized groups: 32 rows x 128 weight rows, four wavefronts of 32 rows
+// x 32 weight rows, two blocks per CU, 128-deep stages (128-byte fp8 or
+// 256-byte bf16 weight-row requests, four MFMA sub-steps per stage) in a ring
+// of two or three.  The weights stream through the LDS ring, so a block keeps
+// its next stage in flight without holding it in registers.
 #ifndef MOE_SMALL_BNW
 #define MOE_SMALL_BNW 128     // build-time knobs: block width and blocks per CU
 #endif
@@ -772,10 +772,15 @@ hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, int 
 hipError_t dispatch_small(const GArgs& g, bool gated, int w_dtype, int out_dtype, int a_dtype,
                           hipStream_t s) {
   using C = Cfg<32, MOE_SMALL_BNW, 1, 4, MOE_SMALL_BPC, true, MOE_SMALL_BK, 16>;
+  using CB = Cfg<32, MOE_SMALL_BNW, 1, 4, MOE_SMALL_BPC, false, MOE_SMALL_BK, 16>;
   for (int i = 0; i < g.nsets; ++i)
     if ((g.s[i].K / (g.s[i].ksplit > 1 ? g.s[i].ksplit : 1)) % C::BK) return hipErrorInvalidValue;
-  if (a_dtype != DT_BF16 || w_dtype != DT_FP8 || out_dtype != DT_BF16) return hipErrorInvalidValue;
-  return gated ? launch_one<C, true, DT_FP8, DT_BF16>(g, s) : launch_one<C, false, DT_FP8, DT_BF16>(g, s);
+  if (a_dtype != DT_BF16 || out_dtype != DT_BF16) return hipErrorInvalidValue;
+  if (w_dtype == DT_FP8)
+    return gated ? launch_one<C, true, DT_FP8, DT_BF16>(g, s) : launch_one<C, false, DT_FP8, DT_BF16>(g, s);
+  if (w_dtype == DT_BF16)
+    return gated ? launch_one<CB, true, DT_BF16, DT_BF16>(g, s) : launch_one<CB, false, DT_BF16, DT_BF16>(g, s);
+  return hipErrorInvalidValue;
 }
 
 // weight rows per block of a shape
