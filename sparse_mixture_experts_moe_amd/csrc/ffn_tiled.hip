@@ -224,13 +224,23 @@ __device__ __forceinline__ bool remap_block(const GArgs& g, int& logical) {
   if (slot >= per_xcd) return false;
   int l = (b % NXCD) * per_xcd + slot;
   if (l >= real) return false;
-  // back to the grid numbering resolve_block uses (valid tiles of each set first)
+  // back to the grid numbering resolve_block uses: the l-th valid (tile, N
+  // block, K slice) of a set, in the set's block order
   for (int i = 0; i < g.nsets; ++i) {
     const GSet& S = g.s[i];
     const int m = S.tiles ? min(S.n_tiles[0], S.m_slots) : S.m_slots;
-    const int n = m * S.blocks_per_m * (S.ksplit > 1 ? S.ksplit : 1);
+    const int ks = S.ksplit > 1 ? S.ksplit : 1;
+    const int n = m * S.blocks_per_m * ks;
     if (l < n) {
-      logical = S.block0 + l;
+      const int pair = l / ks, split = l - pair * ks;
+      int local;
+      if (S.nmajor) {          // N block by N block, the valid tiles of each
+        const int nb = pair / m;
+        local = nb * S.m_slots + (pair - nb * m);
+      } else {                 // tile by tile: the valid tiles come first
+        local = pair;
+      }
+      logical = S.block0 + local * ks + split;
       return true;
     }
     l -= n;
