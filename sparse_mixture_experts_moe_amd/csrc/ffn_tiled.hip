@@ -112,7 +112,7 @@ struct Cfg {
   static constexpr int P = AL + BL;
   static constexpr int P1 = (P + H - 1) / H;          // copies issued per sub-step (the last chunk fewer)
   static_assert(AL * NW * 1024 == A_BYTES && BL * NW * 1024 == B_BYTES, "copy split");
-  static_assert(H == 1 || H == 2 || H == 4, "stage depth");
+  static_assert(H == 1 || H == 2 || H == 4 || H == 8, "stage depth");
   static_assert(S >= 3 || (S == 2 && H >= 2), "ring depth");
   static_assert(TF * WF * MF * MF / 64 * WPE <= 256, "accumulators fit the AGPRs");
   static_assert(WPE == 1 || WPE == 2, "one or two wavefronts per SIMD");
@@ -656,22 +656,26 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   asm volatile("" ::: "memory");
   readf(F0, 0);
   // nst * H sub-steps, a multiple of 2 and of H (with one sub-step per stage,
-  // nst is even: checked by the launcher)
-  using Ph0 = std::integral_constant<int, 0>;
-  using Ph1 = std::integral_constant<int, 1 % H>;
-  using Ph2 = std::integral_constant<int, 2 % H>;
-  using Ph3 = std::integral_constant<int, 3 % H>;
-  if constexpr (H == 4) {
-    for (int t = 0; t < nst * H; t += 4) {
-      step(F0, F1, t, Ph0());
-      step(F1, F0, t + 1, Ph1());
-      step(F0, F1, t + 2, Ph2());
-      step(F1, F0, t + 3, Ph3());
+  // nst is even: checked by the launcher); one loop trip covers UNR of them,
+  // each with its phase known at compile time
+  constexpr int UNR = H > 2 ? H : 2;
+  auto sub = [&](int t, auto ic) __attribute__((always_inline)) {   // sub-step t + I of a trip
+    constexpr int I = decltype(ic)::value;
+    if constexpr (I % 2 == 0) step(F0, F1, t + I, std::integral_constant<int, I % H>());
+    else step(F1, F0, t + I, std::integral_constant<int, I % H>());
+  };
+  for (int t = 0; t < nst * H; t += UNR) {
+    sub(t, std::integral_constant<int, 0>());
+    sub(t, std::integral_constant<int, 1>());
+    if constexpr (UNR >= 4) {
+      sub(t, std::integral_constant<int, 2>());
+      sub(t, std::integral_constant<int, 3>());
     }
-  } else {
-    for (int t = 0; t < nst * H; t += 2) {
-      step(F0, F1, t, Ph0());
-      step(F1, F0, t + 1, Ph1());
+    if constexpr (UNR >= 8) {
+      sub(t, std::integral_constant<int, 4>());
+      sub(t, std::integral_constant<int, 5>());
+      sub(t, std::integral_constant<int, 6>());
+      sub(t, std::integral_constant<int, 7>());
     }
   }
   wait_vm<0>();   // no copy may still be in flight when the block retires
@@ -779,15 +783,31 @@ hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, int 
 #ifndef MOE_SMALL_BK
 #define MOE_SMALL_BK 128
 #endif
+// bf16 weights, K >= MOE_SMALL_DEEP_K: 256-deep stages instead (0 = never)
+#ifndef MOE_SMALL_DEEP
+#define MOE_SMALL_DEEP 1
+#endif
+#ifndef MOE_SMALL_DEEP_K
+#define MOE_SMALL_DEEP_K 2048
+#endif
 hipError_t dispatch_small(const GArgs& g, bool gated, int w_dtype, int out_dtype, int a_dtype,
                           hipStream_t s) {
   using C = Cfg<32, MOE_SMALL_BNW, 1, 4, MOE_SMALL_BPC, true, MOE_SMALL_BK, 16>;
   using CB = Cfg<32, MOE_SMALL_BNW, 1, 4, MOE_SMALL_BPC, false, MOE_SMALL_BK, 16>;
-  for (int i = 0; i < g.nsets; ++i)
-    if ((g.s[i].K / (g.s[i].ksplit > 1 ? g.s[i].ksplit : 1)) % C::BK) return hipErrorInvalidValue;
+  // bf16 weights with a long K: 256-deep stages (512-byte weight-row
+  // requests), one block per CU
+  using CBD = Cfg<32, MOE_SMALL_BNW, 1, 4, 1, false, 256, 16>;
+  bool deep = MOE_SMALL_DEEP && w_dtype == DT_BF16;
+  for (int i = 0; i < g.nsets; ++i) {
+    const int k = g.s[i].K / (g.s[i].ksplit > 1 ? g.s[i].ksplit : 1);
+    if (k % C::BK) return hipErrorInvalidValue;
+    deep = deep && k % CBD::BK == 0 && k >= MOE_SMALL_DEEP_K;
+  }
   if (a_dtype != DT_BF16 || out_dtype != DT_BF16) return hipErrorInvalidValue;
   if (w_dtype == DT_FP8)
     return gated ? launch_one<C, true, DT_FP8, DT_BF16>(g, s) : launch_one<C, false, DT_FP8, DT_BF16>(g, s);
+  if (w_dtype == DT_BF16 && deep)
+    return gated ? launch_one<CBD, true, DT_BF16, DT_BF16>(g, s) : launch_one<CBD, false, DT_BF16, DT_BF16>(g, s);
   if (w_dtype == DT_BF16)
     return gated ? launch_one<CB, true, DT_BF16, DT_BF16>(g, s) : launch_one<CB, false, DT_BF16, DT_BF16>(g, s);
   return hipErrorInvalidValue;
