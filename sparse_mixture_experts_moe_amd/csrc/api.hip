@@ -244,14 +244,23 @@ Plan router_plan(const moe_problem_t* p) {
 }
 
 // K slices of the router: enough work items (tiled blocks or stream
-// wavefronts) to cover the GPU, each slice a multiple of 64 and >= 256 long.
+// wavefronts) to cover the GPU, each slice a multiple of 64 and at least
+// MOE_ROUTER_SLICE long (build-time knobs).
+#ifndef MOE_ROUTER_SLICE
+#define MOE_ROUTER_SLICE 256
+#endif
+#ifndef MOE_ROUTER_ITEMS
+#define MOE_ROUTER_ITEMS 512
+#endif
 int router_splits(const moe_problem_t* p, const Plan& pl) {
   const int64_t m_tiles = (p->T + pl.bm - 1) / pl.bm;
   const int64_t items = pl.tiled ? m_tiles * tiled_blocks_n(TILED_NARROW, false, p->E)
                                  : m_tiles * stream_waves_n(false, p->E);
   int s = 1;
   const int K = p->D;
-  while (K % (2 * s) == 0 && (K / (2 * s)) % 64 == 0 && K / (2 * s) >= 256 && items * s < 512) s *= 2;
+  while (K % (2 * s) == 0 && (K / (2 * s)) % 64 == 0 && K / (2 * s) >= MOE_ROUTER_SLICE &&
+         items * s < MOE_ROUTER_ITEMS)
+    s *= 2;
   return s;
 }
 
@@ -492,7 +501,7 @@ moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_
   StageScope sc(ST_PERMUTE, s);
   if (p->T <= perm_small_max_tokens()) {
     MOE_LAUNCH(launch_permute_small(topk_idx, p->T, p->k, p->E, counts, offsets, row_token,
-                                    row_of_slot, 1, 0, nullptr, nullptr, s));
+                                    row_of_slot, 1, 0, false, nullptr, nullptr, s));
   } else {
     MOE_LAUNCH(launch_permute(topk_idx, p->T, p->k, p->E, reinterpret_cast<int32_t*>(w + L.blk),
                               reinterpret_cast<int32_t*>(w + L.rank), counts, offsets, row_token,
@@ -681,7 +690,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
   if (p->T <= perm_small_max_tokens() && (!pl.tiled || pl.shape == TILED_SMALL)) {
     StageScope sc(ST_PERMUTE, s);
     MOE_LAUNCH(launch_permute_small(idx, p->T, p->k, p->E, counts, offsets, row_token, row_of_slot,
-                                    pl.bm, L.tile_ub, tiles, ntiles, s));
+                                    pl.bm, L.tile_ub, pl.tiled, tiles, ntiles, s));
   } else {
     {
       StageScope sc(ST_PERMUTE, s);

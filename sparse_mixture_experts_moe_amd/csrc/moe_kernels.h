@@ -158,11 +158,13 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* blk 
                           int32_t* row_token, int32_t* row_of_slot, hipStream_t s);
 
 // Batches of at most perm_small_max_tokens() tokens: permutation and, when
-// tiles is not null, the M-tile table (group order) in one single-block launch.
+// tiles is not null, the M-tile table (group order or, spread, a fixed order
+// that puts neighbouring groups far apart) in one single-block launch.
 int perm_small_max_tokens();
 hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int32_t* counts,
                                 int32_t* offsets, int32_t* row_token, int32_t* row_of_slot, int bm,
-                                int max_tiles, GTile* tiles, int32_t* n_tiles, hipStream_t s);
+                                int max_tiles, bool spread, GTile* tiles, int32_t* n_tiles,
+                                hipStream_t s);
 
 // M-tile table of n_groups groups from device offsets, in group order or, with
 // largest_first, by descending group size (ties by group id).  Offsets are

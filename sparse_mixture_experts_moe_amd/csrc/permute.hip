@@ -174,8 +174,8 @@ __global__ __launch_bounds__(TILE_THREADS) void build_tiles_kernel(const int32_t
   }
 }
 
-// Batches of at most PB tokens (decode): the whole permutation and the M-tile
-// table (in group order) in one block, with the same bit-mask ranking.
+// Batches of at most 1024 tokens (decode): the whole permutation and the
+// M-tile table (in group order) in one block, with the same bit-mask ranking.
 __device__ __forceinline__ int block_inclusive_scan(int32_t* sc, int v) {
   const int i = threadIdx.x;
   sc[i] = v;
@@ -189,10 +189,23 @@ __device__ __forceinline__ int block_inclusive_scan(int32_t* sc, int v) {
   return sc[i];
 }
 
+// Order of the groups' M-tiles when spread: 1 = a stride permutation of the
+// group ids (measured faster: concurrently running blocks then stream weights
+// from experts far apart), 0 = largest group first.
+#ifndef MOE_PERM_SCRAMBLE
+#define MOE_PERM_SCRAMBLE 1
+#endif
+#ifndef MOE_PERM_STRIDE_NUM      // stride of the group order: about NUM / DEN of E
+#define MOE_PERM_STRIDE_NUM 1
+#define MOE_PERM_STRIDE_DEN 2
+#endif
+// MW 64-bit mask words per expert: batches of at most 64 * MW tokens.
+template <int MW>
 __global__ __launch_bounds__(SCAN_THREADS) void perm_small_kernel(
     const int32_t* __restrict__ idx, int T, int k, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ row_of_slot,
-    int bm, int max_tiles, GTile* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+    int bm, int max_tiles, int spread, GTile* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  constexpr int WORDS = MW;
   __shared__ unsigned long long mask[SCAN_THREADS * WORDS];   // [E][WORDS]
   __shared__ int32_t sc[SCAN_THREADS];
   __shared__ int32_t off_s[SCAN_THREADS + 1];
@@ -236,16 +249,52 @@ __global__ __launch_bounds__(SCAN_THREADS) void perm_small_kernel(
     row_of_slot[a] = r;
   }
   if (!tiles) return;
-  // M-tiles of each group, groups in id order
-  const int nt = tid < E ? (c + bm - 1) / bm : 0;
+  // M-tiles of each group: groups in id order or, spread, in a fixed order
+  // that puts neighbouring groups far apart
+  __shared__ int32_t sz[SCAN_THREADS];
+  __shared__ int32_t grp[SCAN_THREADS];
+  sz[tid] = tid < E ? c : 0;
+  __syncthreads();
+  int rank = tid;
+#if MOE_PERM_SCRAMBLE
+  if (spread && tid < E) {
+    // a fixed stride permutation of the groups: a stride of about E / 2, made
+    // coprime to E, so neighbouring groups land far apart in the order
+    // (odd start, steps of 2: reaches a unit mod E, so the search ends)
+    int a = (MOE_PERM_STRIDE_NUM * E / MOE_PERM_STRIDE_DEN + 1) | 1;
+    for (;;) {
+      int x = a, y = E;
+      while (y) {
+        const int t = x % y;
+        x = y;
+        y = t;
+      }
+      if (x == 1) break;
+      a += 2;
+    }
+    rank = static_cast<int>((static_cast<int64_t>(tid) * a) % E);
+  }
+#else
+  if (spread && tid < E) {   // largest group first (ties by id)
+    rank = 0;
+    for (int o = 0; o < E; ++o) {
+      const int no = sz[o];
+      rank += (no > c) || (no == c && o < tid);
+    }
+  }
+#endif
+  if (tid < E) grp[rank] = tid;
+  __syncthreads();
+  const int gg = tid < E ? grp[tid] : 0;           // group at rank position tid
+  const int nt = tid < E ? (sz[gg] + bm - 1) / bm : 0;
   const int tincl = block_inclusive_scan(sc, nt);
   if (tid < E) {
     const int base = tincl - nt;
     for (int i = 0; i < nt && base + i < max_tiles; ++i) {
       GTile tl;
-      tl.group = tid;
-      tl.row0 = off_s[tid] + i * bm;
-      tl.row1 = min(off_s[tid] + (i + 1) * bm, off_s[tid + 1]);
+      tl.group = gg;
+      tl.row0 = off_s[gg] + i * bm;
+      tl.row1 = min(off_s[gg] + (i + 1) * bm, off_s[gg + 1]);
       tl.pad = 0;
       tiles[base + i] = tl;
     }
@@ -257,13 +306,23 @@ __global__ __launch_bounds__(SCAN_THREADS) void perm_small_kernel(
 
 int perm_blocks(int T) { return (T + PB - 1) / PB; }
 
-int perm_small_max_tokens() { return PB; }
+int perm_small_max_tokens() { return 16 * 64; }
 
 hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int32_t* counts,
                                 int32_t* offsets, int32_t* row_token, int32_t* row_of_slot, int bm,
-                                int max_tiles, GTile* tiles, int32_t* n_tiles, hipStream_t s) {
-  perm_small_kernel<<<1, SCAN_THREADS, 0, s>>>(idx, T, k, E, counts, offsets, row_token, row_of_slot,
-                                               bm, max_tiles, tiles, n_tiles);
+                                int max_tiles, bool spread, GTile* tiles, int32_t* n_tiles,
+                                hipStream_t s) {
+  if (T > perm_small_max_tokens()) return hipErrorInvalidValue;
+  const int lf = spread ? 1 : 0;
+  if (T <= 4 * 64)
+    perm_small_kernel<4><<<1, SCAN_THREADS, 0, s>>>(idx, T, k, E, counts, offsets, row_token,
+                                                    row_of_slot, bm, max_tiles, lf, tiles, n_tiles);
+  else if (T <= 8 * 64)
+    perm_small_kernel<8><<<1, SCAN_THREADS, 0, s>>>(idx, T, k, E, counts, offsets, row_token,
+                                                    row_of_slot, bm, max_tiles, lf, tiles, n_tiles);
+  else
+    perm_small_kernel<16><<<1, SCAN_THREADS, 0, s>>>(idx, T, k, E, counts, offsets, row_token,
+                                                     row_of_slot, bm, max_tiles, lf, tiles, n_tiles);
   return hipGetLastError();
 }
 

@@ -30,6 +30,9 @@ SMALL = {
     # and experts over 32 rows): the automatic policy's 32-row tiled shape
     "ling_decode_like": shrink(CONFIGS["ling_decode"], T=200, D=512, E=64, k=4, I=256, I_shared=256,
                                zipf=True),
+    # bf16 decode with K = D = 2304 on the gate/up projection: the 32-row
+    # shape's 256-deep stages (9 of them), 128-deep ones on the down projection
+    "qwen_decode_deep": shrink(CONFIGS["qwen_decode"], T=40, D=2304, E=32, k=6, I=384, I_shared=128),
 }
 
 
@@ -215,8 +218,8 @@ def test_moe_route_ties_and_signed_zero():
     assert np.allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=0)
 
 
-@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (255, 16, 4), (256, 16, 4), (1000, 512, 10),
-                                   (4099, 256, 8), (600, 1024, 32)])
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (255, 16, 4), (256, 16, 4), (300, 64, 4), (1000, 512, 10),
+                                   (1024, 1024, 8), (1025, 64, 2), (4099, 256, 8), (600, 1024, 32)])
 def test_moe_permute_entry(T, E, k):
     rng = np.random.default_rng(T + E)
     idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
@@ -251,7 +254,8 @@ def test_moe_combine_reproduces_gathered_rows():
 
 
 @pytest.mark.parametrize("policy", ["stream", "lds", "auto"])
-@pytest.mark.parametrize("name", ["qwen_ragged", "ling_fp8", "gemma_like", "ling_decode_like"])
+@pytest.mark.parametrize("name", ["qwen_ragged", "ling_fp8", "gemma_like", "ling_decode_like",
+                                  "qwen_decode_deep"])
 def test_moe_grouped_ffn_entry(name, policy):
     """Grouped FFN alone on permuted rows, and the shared branch as one group."""
     cfg = SMALL[name]
