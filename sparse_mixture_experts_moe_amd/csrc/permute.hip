@@ -109,6 +109,32 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
   row_of_slot[a] = r;
 }
 
+#ifndef MOE_PERM_STRIDE_NUM      // stride of the spread group order: about NUM / DEN of E
+#define MOE_PERM_STRIDE_NUM 1
+#define MOE_PERM_STRIDE_DEN 2
+#endif
+// Position of group g (< G) in a fixed stride permutation of the groups: a
+// stride of about G / 2, made coprime to G, so neighbouring groups land far
+// apart in the order.  (Odd start, steps of 2: the search reaches a unit mod
+// G, so it ends.)
+__device__ __forceinline__ int spread_rank(int g, int G) {
+  int a = (MOE_PERM_STRIDE_NUM * G / MOE_PERM_STRIDE_DEN + 1) | 1;
+  for (;;) {
+    int x = a, y = G;
+    while (y) {
+      const int t = x % y;
+      x = y;
+      y = t;
+    }
+    if (x == 1) break;
+    a += 2;
+  }
+  return static_cast<int>((static_cast<int64_t>(g) * a) % G);
+}
+#ifndef MOE_TILES_SPREAD         // 1: the multi-block path's tile table in the spread order too
+#define MOE_TILES_SPREAD 0
+#endif
+
 // Single block: each group's M-tiles.  With largest_first the groups are
 // ordered by descending row count (ties by group id) so the heaviest experts
 // start first; otherwise in group order.
@@ -134,11 +160,15 @@ __global__ __launch_bounds__(TILE_THREADS) void build_tiles_kernel(const int32_t
   __syncthreads();
   int rank = g;
   if (largest_first && g < G) {
+#if MOE_TILES_SPREAD
+    rank = spread_rank(g, G);
+#else
     rank = 0;
     for (int o = 0; o < G; ++o) {
       const int no = sz[o];
       rank += (no > n) || (no == n && o < g);
     }
+#endif
   }
   ntl[g] = 0;
   __syncthreads();
@@ -194,10 +224,6 @@ __device__ __forceinline__ int block_inclusive_scan(int32_t* sc, int v) {
 // from experts far apart), 0 = largest group first.
 #ifndef MOE_PERM_SCRAMBLE
 #define MOE_PERM_SCRAMBLE 1
-#endif
-#ifndef MOE_PERM_STRIDE_NUM      // stride of the group order: about NUM / DEN of E
-#define MOE_PERM_STRIDE_NUM 1
-#define MOE_PERM_STRIDE_DEN 2
 #endif
 // MW 64-bit mask words per expert: batches of at most 64 * MW tokens.
 template <int MW>
@@ -257,23 +283,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void perm_small_kernel(
   __syncthreads();
   int rank = tid;
 #if MOE_PERM_SCRAMBLE
-  if (spread && tid < E) {
-    // a fixed stride permutation of the groups: a stride of about E / 2, made
-    // coprime to E, so neighbouring groups land far apart in the order
-    // (odd start, steps of 2: reaches a unit mod E, so the search ends)
-    int a = (MOE_PERM_STRIDE_NUM * E / MOE_PERM_STRIDE_DEN + 1) | 1;
-    for (;;) {
-      int x = a, y = E;
-      while (y) {
-        const int t = x % y;
-        x = y;
-        y = t;
-      }
-      if (x == 1) break;
-      a += 2;
-    }
-    rank = static_cast<int>((static_cast<int64_t>(tid) * a) % E);
-  }
+  if (spread && tid < E) rank = spread_rank(tid, E);
 #else
   if (spread && tid < E) {   // largest group first (ties by id)
     rank = 0;
