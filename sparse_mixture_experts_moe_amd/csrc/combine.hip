@@ -15,21 +15,37 @@ constexpr int THREADS = 128;
 constexpr int CHUNK = THREADS * 8;   // hidden elements per block
 constexpr int MAXK = 32;
 
+// 8 elements as stored (bf16: 16 bytes; fp32: 32 bytes), loaded without use
+// so that several rows' loads can be in flight together
+template <int DT> struct Raw8;
+template <> struct Raw8<DT_BF16> { uint4 q; };
+template <> struct Raw8<DT_F32> { float4 a, b; };
+
 template <int DT>
-__device__ __forceinline__ void load8(const void* base, int64_t off, float (&v)[8]) {
+__device__ __forceinline__ Raw8<DT> load_raw(const void* base, int64_t off) {
+  Raw8<DT> r;
   if constexpr (DT == DT_BF16) {
-    const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    r.q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    r.a = p[0];
+    r.b = p[1];
+  }
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void widen(const Raw8<DT>& r, float (&v)[8]) {
+  if constexpr (DT == DT_BF16) {
+    const uint32_t w[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       v[2 * i] = __uint_as_float(w[i] << 16);
       v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   } else {
-    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-    const float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+    v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
   }
 }
 
@@ -67,20 +83,36 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const void* __restrict
     const int d = blockIdx.y * CHUNK + threadIdx.x * 8;
     if (d >= D) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = rows[j];
-      if (r < 0) continue;
-      float v[8];
-      load8<DT>(o_perm, static_cast<int64_t>(r) * D + d, v);
-      const float wj = ws[j];
+    Raw8<DT> sraw;
+    if (shared) sraw = load_raw<DT>(shared, static_cast<int64_t>(t) * D + d);
+    // slots in groups of 8: all of a group's loads are issued before the
+    // first is used (a slot past k or without a row reads row 0 and is
+    // skipped), then the rows are added in slot order
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      Raw8<DT> raw[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        const int r = j < k ? rows[j] : -1;
+        raw[u] = load_raw<DT>(o_perm, static_cast<int64_t>(r < 0 ? 0 : r) * D + d);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = j0 + u;
+        if (j < k && rows[j] >= 0) {
+          float v[8];
+          widen<DT>(raw[u], v);
+          const float wj = ws[j];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
+        }
+      }
     }
     if (shared) {
-      float v[8];
-      load8<DT>(shared, static_cast<int64_t>(t) * D + d, v);
+      float sv[8];
+      widen<DT>(sraw, sv);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+      for (int i = 0; i < 8; ++i) acc[i] += sv[i];
     }
     store8<DT>(y, static_cast<int64_t>(t) * D + d, acc);
   }
