@@ -203,6 +203,52 @@ template <int P, int M> __device__ __forceinline__ void wait_newer(int newer) {
 #define MOE_SMALL_NT 0
 #endif
 constexpr int NXCD = 8;   // XCDs; workgroup i is dispatched to XCD i % NXCD
+// Block order of the 256-row shape (MOE_TILED_XCDTILE 1): all N blocks of an
+// M-tile on one XCD (tile t on XCD t % NXCD), tiles interleaved across the
+// XCDs, so a tile's activation rows are fetched into one L2 instead of eight.
+// The default order puts N block n of every tile on XCD n, which instead
+// shares an expert's weight slabs between its tiles: better where experts
+// have several tiles (the 128-row shapes, measured), worse where most have
+// one (the 256-row shape: Qwen prefill 4.73 -> 4.61 ms, Gemma level).
+#ifndef MOE_TILED_XCDTILE
+#define MOE_TILED_XCDTILE 1
+#endif
+template <class C> constexpr bool xcdtile() { return MOE_TILED_XCDTILE && C::BM == 256; }
+
+#if MOE_TILED_XCDTILE
+// The XCD-tile order applies to grids without K slices or N-major sets.
+__host__ __device__ inline bool xcdtile_ok(const GArgs& g) {
+  for (int i = 0; i < g.nsets; ++i)
+    if (g.s[i].ksplit > 1 || g.s[i].nmajor) return false;
+  return true;
+}
+// Physical grid of the XCD-tile order: each set's tiles padded to a multiple
+// of NXCD, all of a tile's N blocks.
+__host__ __device__ inline int xcdtile_grid(const GArgs& g) {
+  int n = 0;
+  for (int i = 0; i < g.nsets; ++i)
+    n += (g.s[i].m_slots + NXCD - 1) / NXCD * NXCD * g.s[i].blocks_per_m;
+  return n;
+}
+// Logical block (resolve_block's numbering, tile-major) of physical block b
+// in the XCD-tile order; false if b has no tile.
+__device__ __forceinline__ bool xcdtile_block(const GArgs& g, int b, int& logical) {
+  for (int i = 0; i < g.nsets; ++i) {
+    const GSet& S = g.s[i];
+    const int bpm = S.blocks_per_m;
+    const int seg = (S.m_slots + NXCD - 1) / NXCD * NXCD * bpm;   // a multiple of NXCD
+    if (b < seg) {
+      const int x = b % NXCD, q = b / NXCD;
+      const int tile = x + NXCD * (q / bpm), n = q % bpm;
+      if (tile >= S.m_slots) return false;
+      logical = S.block0 + tile * bpm + n;
+      return true;
+    }
+    b -= seg;
+  }
+  return false;
+}
+#endif
 template <class C> constexpr bool remapped() { return MOE_TILED_REMAP || (MOE_SMALL_REMAP && C::BM == 32); }
 
 #if MOE_TILED_REMAP || MOE_SMALL_REMAP
@@ -262,6 +308,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   // the VGPRs stay free for fragments.
   asm volatile("" ::: "a0");
   int b = blockIdx.x;
+#if MOE_TILED_XCDTILE
+  if constexpr (xcdtile<C>())
+    if (xcdtile_ok(g) && !xcdtile_block(g, blockIdx.x, b)) return;
+#endif
 #if MOE_TILED_REMAP || MOE_SMALL_REMAP
   if constexpr (remapped<C>())
     if (!remap_block(g, b)) return;
@@ -730,7 +780,11 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
 
 template <class C, bool GATED, int WDT, int ODT>
 hipError_t launch_one(const GArgs& g, hipStream_t s) {
-  const int grid = remapped<C>() ? (g.total_blocks + NXCD - 1) / NXCD * NXCD : g.total_blocks;
+  int grid = remapped<C>() ? (g.total_blocks + NXCD - 1) / NXCD * NXCD : g.total_blocks;
+#if MOE_TILED_XCDTILE
+  if constexpr (xcdtile<C>())
+    if (xcdtile_ok(g)) grid = xcdtile_grid(g);
+#endif
   tiled_gemm_kernel<C, GATED, WDT, ODT><<<grid, C::THREADS, 0, s>>>(g);
   return hipGetLastError();
 }
