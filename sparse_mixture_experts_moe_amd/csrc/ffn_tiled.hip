@@ -213,9 +213,14 @@ constexpr int NXCD = 8;   // XCDs; workgroup i is dispatched to XCD i % NXCD
 #ifndef MOE_TILED_XCDTILE
 #define MOE_TILED_XCDTILE 1
 #endif
-template <class C> constexpr bool xcdtile() { return MOE_TILED_XCDTILE && C::BM == 256; }
+#ifndef MOE_SMALL_XCDTILE       // the same order for the 32-row shape
+#define MOE_SMALL_XCDTILE 0
+#endif
+template <class C> constexpr bool xcdtile() {
+  return (MOE_TILED_XCDTILE && C::BM == 256) || (MOE_SMALL_XCDTILE && C::BM == 32);
+}
 
-#if MOE_TILED_XCDTILE
+#if MOE_TILED_XCDTILE || MOE_SMALL_XCDTILE
 // The XCD-tile order applies to grids without K slices or N-major sets.
 __host__ __device__ inline bool xcdtile_ok(const GArgs& g) {
   for (int i = 0; i < g.nsets; ++i)
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   // the VGPRs stay free for fragments.
   asm volatile("" ::: "a0");
   int b = blockIdx.x;
-#if MOE_TILED_XCDTILE
+#if MOE_TILED_XCDTILE || MOE_SMALL_XCDTILE
   if constexpr (xcdtile<C>())
     if (xcdtile_ok(g) && !xcdtile_block(g, blockIdx.x, b)) return;
 #endif
@@ -781,7 +786,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
 template <class C, bool GATED, int WDT, int ODT>
 hipError_t launch_one(const GArgs& g, hipStream_t s) {
   int grid = remapped<C>() ? (g.total_blocks + NXCD - 1) / NXCD * NXCD : g.total_blocks;
-#if MOE_TILED_XCDTILE
+#if MOE_TILED_XCDTILE || MOE_SMALL_XCDTILE
   if constexpr (xcdtile<C>())
     if (xcdtile_ok(g)) grid = xcdtile_grid(g);
 #endif
