@@ -64,9 +64,11 @@ extern "C" {
 #define MOE_ACT_GELU_TANH  1   /* GEGLU:  tanh-GELU(gate) * up       */
 
 /* tile policies of the grouped FFN */
-#define MOE_TILE_AUTO     0    /* chosen on the host from T*k/E            */
-#define MOE_TILE_STREAM   1    /* register-streamed weights, small groups  */
-#define MOE_TILE_LDS      2    /* LDS-tiled MFMA GEMM, large groups         */
+#define MOE_TILE_AUTO     0    /* chosen on the host from T*k/E, the weight
+                                  format and the sizes (decode batches: 32-row
+                                  LDS-tiled blocks; prefill: 128 / 256-row)  */
+#define MOE_TILE_STREAM   1    /* register-streamed weights, no LDS         */
+#define MOE_TILE_LDS      2    /* LDS-tiled MFMA GEMM, 128 / 256-row tiles   */
 
 /* activation quantisation of the expert GEMMs (moe_problem_t.act_quant) */
 #define MOE_ACT_QUANT_NONE     0   /* bf16 activations                       */

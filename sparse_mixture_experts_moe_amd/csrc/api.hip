@@ -117,7 +117,8 @@ struct Plan {
   bool tiled;  // LDS-tiled kernel
   int mt;      // stream kernel: 16-row chunks per m-tile
   int bm;      // rows per m-tile
-  int shape;   // tiled kernel: TILED_TALL, or -1 = wide / narrow picked per launch
+  int shape;   // tiled kernel: TILED_TALL / TILED_SMALL / TILED_WIDE, or -1 = wide /
+               // narrow picked per launch
 };
 
 constexpr bool kTiledReady = true;
