@@ -104,10 +104,14 @@ def test_layer_is_deterministic():
 
 
 @pytest.mark.parametrize("over", [dict(T=1), dict(T=3, E=64), dict(E=8, k=8), dict(T=257),
-                                  dict(T=513, k=1)])
+                                  dict(T=513, k=1),
+                                  # I = 128: the 32-row tiled shape (decode plans), with the
+                                  # one-launch permutation at 4, 8 and 16 mask words
+                                  dict(T=1, I=128), dict(T=300, E=64, k=6, I=128),
+                                  dict(T=700, E=32, k=2, I=128), dict(T=1000, E=256, k=8, I=128)])
 def test_layer_edge_shapes(over):
-    cfg = shrink(CONFIGS["qwen_decode"], D=128, E=over.get("E", 16), k=over.get("k", 4), I=64,
-                 I_shared=64, T=over["T"] if "T" in over else 40)
+    cfg = shrink(CONFIGS["qwen_decode"], D=128, E=over.get("E", 16), k=over.get("k", 4),
+                 I=over.get("I", 64), I_shared=64, T=over["T"] if "T" in over else 40)
     wl = to_device(generate(cfg, seed=4))
     ref = oracle_layer(wl)
     res = run_layer(wl, logits_in=torch.from_numpy(ref["logits"]).cuda())
