@@ -4,6 +4,10 @@
 // bound by reading every touched expert's weights once ("Qwen 3.5 MoE on
 // Ironwood", roofline section: decode is HBM-bound at about 1 FLOP/byte; the
 // "Ling-2.6-1T with SGLang-JAX" page, section 1, HBM weight-movement bound).
+// The automatic tile policy runs most decode batches on the LDS-tiled
+// kernel's 32-row shape instead, which keeps more weight bytes in flight; this
+// kernel serves the fp32 layer, the decode router, sizes that shape does not
+// take and the MOE_TILE_STREAM policy.
 //
 // Work decomposition: each 64-wide wavefront owns one M-tile of a group (up to
 // 16*MT sorted rows) and 64 weight rows (4 MFMA fragments of 16).  For the

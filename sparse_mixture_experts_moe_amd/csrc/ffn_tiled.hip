@@ -1,4 +1,5 @@
-// LDS-tiled grouped GEMM for large groups (prefill-sized batches).
+// LDS-tiled grouped GEMM: prefill-sized groups, and decode batches in a
+// 32-row shape.
 //
 // Prefill is bound by the MFMA units once every expert has hundreds of rows
 // ("Qwen 3.5 MoE on Ironwood", roofline section: prefill is compute-bound and
@@ -6,14 +7,16 @@
 // "Ling-2.6-1T with SGLang-JAX", section 4: keep tokens and accumulators
 // resident and stream the expert weights with the next tile's fetch in flight).
 //
-// Block tile: BM sorted rows of one group x BNW weight rows, in three shapes:
+// Block tile: BM sorted rows of one group x BNW weight rows, in four shapes:
 // "tall" (256 x 256, 8 wavefronts, one block per CU) for the expert FFNs -- an
 // expert's weights are read once per 256 rows, and the row fragments a short
 // tile does not fill are skipped --, "wide" (128 x 512, 8 wavefronts) and
-// "narrow" (128 x 256, 4 wavefronts, two blocks per CU) for dense products such
-// as the router.  In all of them every SIMD runs two wavefronts of 64 rows x 128
-// weight rows (128 accumulators each, in AGPRs), which is what it takes to keep
-// the matrix cores busy; 16x16x32 bf16 MFMAs take the weight fragment as the M
+// "narrow" (128 x 256, 4 wavefronts, two blocks per CU) for larger groups and
+// dense products such as the router, and "small" (32 x 128, 4 wavefronts of
+// 32 x 32, two blocks per CU) for decode batches, where the weights only need
+// to stream through.  In the first three every SIMD runs two wavefronts of 64
+// rows x 128 weight rows (128 accumulators each, in AGPRs), which is what it
+// takes to keep the matrix cores busy; 16x16x32 bf16 MFMAs take the weight fragment as the M
 // operand, so a lane's accumulator holds 4 consecutive output columns of one
 // row.  For the fused gate/up projection the BNW weight rows are BNW/2 gate
 // rows and the matching BNW/2 up rows; each wavefront holds the gate and up
@@ -35,6 +38,15 @@
 // matrix cores; fp8 weights are therefore staged 64 deep (64-byte weight and
 // 128-byte activation segments, half the requests per FLOP).  bf16 tiles stay
 // 32 deep, where a deeper stage would leave fewer than three in the LDS ring.
+// The small shape stages 128 deep (256 deep for bf16 weights over a long K),
+// so its weight-row requests are 128 to 512 bytes; a stage then spans four or
+// eight MFMA sub-steps, its copies spread over them.
+//
+// Workgroup b runs on XCD b % 8, and each XCD has its own L2: the 256-row
+// shape maps all N blocks of an M-tile to one XCD (tiles interleaved across
+// XCDs) so the tile's activation rows are fetched once; the other shapes keep
+// N block n of every tile on XCD n, which shares an expert's weight slab
+// between its tiles.
 //
 // With fp8 activations as well (dynamic per-token quantisation, "Ling-2.6-1T
 // with SGLang-JAX" page, section 5: fp8 tokens and fp8 weights straight into
