@@ -169,8 +169,9 @@ bool tiled_fits(const moe_problem_t* p) {
 
 Plan make_plan(const moe_problem_t* p, double mean_rows) {
   if (quantised(p)) {
-    // fp8 x fp8, MXFP8 x MXFP4: the tiled kernel's one-block-per-CU shapes
-    const int shape = mean_rows <= MOE_TALL_MEAN ? TILED_TALL : TILED_WIDE;
+    // fp8 x fp8, MXFP8 x MXFP4: the tiled kernel's quantised shapes
+    const int shape = (MOE_TILED_SMALL && mean_rows <= MOE_SMALL_MAX) ? TILED_SMALLQ
+                      : mean_rows <= MOE_TALL_MEAN ? TILED_TALL : TILED_WIDE;
     return Plan{true, 0, tiled_bm(shape), shape};
   }
   const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16 && tiled_fits(p);
@@ -688,7 +689,8 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
                                    idx, tw, s));
   }
   // 2. permutation and the M-tile table (one launch for small batches)
-  if (p->T <= perm_small_max_tokens() && (!pl.tiled || pl.shape == TILED_SMALL)) {
+  if (p->T <= perm_small_max_tokens() &&
+      (!pl.tiled || pl.shape == TILED_SMALL || pl.shape == TILED_SMALLQ)) {
     StageScope sc(ST_PERMUTE, s);
     MOE_LAUNCH(launch_permute_small(idx, p->T, p->k, p->E, counts, offsets, row_token, row_of_slot,
                                     pl.bm, L.tile_ub, pl.tiled, tiles, ntiles, s));

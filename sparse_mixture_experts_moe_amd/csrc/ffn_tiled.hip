@@ -884,6 +884,22 @@ hipError_t dispatch_small(const GArgs& g, bool gated, int w_dtype, int out_dtype
   return hipErrorInvalidValue;
 }
 
+// Decode-sized groups with quantised activations: 64 rows x 256 weight rows,
+// four wavefronts of 64 x 64 (one 32 x 32 fragment pair of gate and up rows
+// each), two blocks per CU, 128-deep stages; fp8 x fp8, or MXFP8 x MXFP4 with
+// the block-scale tiles.
+hipError_t dispatch_smallq(const GArgs& g, bool gated, int w_dtype, int out_dtype, int a_dtype,
+                           hipStream_t s) {
+  using CA = Cfg<64, 256, 1, 4, 2, true, 128, 32, true>;
+  using CW = Cfg<64, 256, 1, 4, 2, true, 128, 32, true, true>;
+  if (out_dtype != DT_BF16) return hipErrorInvalidValue;
+  if (a_dtype == DT_FP8 && w_dtype == DT_FP8)
+    return gated ? launch_one<CA, true, DT_FP8, DT_BF16>(g, s) : launch_one<CA, false, DT_FP8, DT_BF16>(g, s);
+  if (a_dtype == DT_MXFP8 && w_dtype == DT_MXFP4)
+    return gated ? launch_one<CW, true, DT_MXFP4, DT_BF16>(g, s) : launch_one<CW, false, DT_MXFP4, DT_BF16>(g, s);
+  return hipErrorInvalidValue;
+}
+
 // weight rows per block of a shape
 int block_width(int shape) {
   return shape == TILED_WIDE ? 512 : shape == TILED_SMALL ? MOE_SMALL_BNW : 256;
@@ -891,7 +907,9 @@ int block_width(int shape) {
 
 }  // namespace
 
-int tiled_bm(int shape) { return shape == TILED_TALL ? 256 : shape == TILED_SMALL ? 32 : 128; }
+int tiled_bm(int shape) {
+  return shape == TILED_TALL ? 256 : shape == TILED_SMALL ? 32 : shape == TILED_SMALLQ ? 64 : 128;
+}
 
 int tiled_k_multiple() { return 2 * KS; }
 
@@ -928,6 +946,7 @@ hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype,
     case TILED_WIDE: return dispatch<128, 512, 2, 4, 1, 16>(g, gated, w_dtype, out_dtype, a_dtype, s);
     case TILED_NARROW: return dispatch<128, 256, 2, 2, 2, 16>(g, gated, w_dtype, out_dtype, a_dtype, s);
     case TILED_SMALL: return dispatch_small(g, gated, w_dtype, out_dtype, a_dtype, s);
+    case TILED_SMALLQ: return dispatch_smallq(g, gated, w_dtype, out_dtype, a_dtype, s);
   }
   return hipErrorInvalidValue;
 }

@@ -184,9 +184,10 @@ int stream_max_mt(int a_dtype);              // largest mt the stream kernel run
 // Grouped GEMM, LDS-tiled (bf16 activations, bf16 or fp8 weights).  Block
 // shapes (rows x weight rows): TILED_TALL 256 x 256 (expert FFNs), TILED_WIDE
 // 128 x 512 and TILED_NARROW 128 x 256 (two blocks per CU), TILED_SMALL
-// 32 x 128 (two blocks per CU; decode-sized groups).  Every set's bm must be
-// tiled_bm(shape).
-enum : int { TILED_TALL = 0, TILED_WIDE = 1, TILED_NARROW = 2, TILED_SMALL = 3 };
+// 32 x 128 (two blocks per CU; decode-sized groups), TILED_SMALLQ 64 x 256
+// (two blocks per CU; decode-sized groups with fp8 or MXFP8 activations).
+// Every set's bm must be tiled_bm(shape).
+enum : int { TILED_TALL = 0, TILED_WIDE = 1, TILED_NARROW = 2, TILED_SMALL = 3, TILED_SMALLQ = 4 };
 // a_dtype DT_FP8 (fp8 activations with fp8 weights, bf16 output, one block
 // per CU shapes only) needs every set's a_scale; a_dtype DT_MXFP8 (with
 // DT_MXFP4 weights, same shapes and output) every set's a_mx and w_mx, with

@@ -62,6 +62,8 @@ SMALL = {
     # more than 256 rows per expert: 128-row tiles with ragged tails
     "big_groups_fp8": shrink(CONFIGS["ling_prefill"], T=1030, D=384, E=4, k=2, I=256, I_shared=128),
     "no_shared": shrink(CONFIGS["ling_decode"], T=77, D=128, E=8, k=3, I=256, I_shared=0),
+    # about 24 rows per expert: the 64-row decode shape, routed and shared sets
+    "decode_fp8": shrink(CONFIGS["ling_decode"], T=96, D=256, E=32, k=8, I=128, I_shared=128),
 }
 
 
