@@ -119,6 +119,27 @@ def test_layer_edge_shapes(over):
     assert rel_err(f64(res["y"]), ref["y"]) <= tol_for(cfg)
 
 
+# 256-row tiles with skewed loads: hot experts with two to four tiles next to
+# one-tile and empty experts, and one expert taking every token (16 tiles)
+@pytest.mark.parametrize("T,k,skew", [(2000, 2, 0.15), (4096, 1, None)])
+def test_layer_skewed_tall_tiles(T, k, skew):
+    cfg = shrink(CONFIGS["qwen_prefill"], T=T, D=256, E=64, k=k, I=64, I_shared=64, zipf=False)
+    print(f"[skewed 256-row tiles] T={T} k={k} skew={skew}", flush=True)
+    wl = to_device(generate(cfg, seed=6))
+    rng = np.random.default_rng(T)
+    logits = rng.standard_normal((T, cfg.E)).astype(np.float32)
+    if skew is None:
+        logits[:, 0] += 100.0
+    else:
+        logits -= np.float32(skew) * np.arange(cfg.E, dtype=np.float32)
+    ref = oracle_layer(wl, logits_in=logits)
+    counts = np.asarray(ref["counts"])
+    assert counts.max() > 256 and (skew is None or np.sum((counts > 0) & (counts <= 256)) > 8)
+    res = run_layer(wl, "lds", logits_in=torch.from_numpy(logits).cuda())
+    _check_routing(res, ref)
+    assert rel_err(f64(res["y"]), ref["y"]) <= tol_for(cfg)
+
+
 # fp32 plain-softmax weight: expf (2 ulp) of each term, a sum of E/64 terms per
 # lane then 6 butterfly levels, and a divide: under 25 ulp (1.5e-6) for E <= 1024
 PLAIN_W_RTOL = 3e-6
