@@ -193,7 +193,8 @@ moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_
  *   E8M0 block scales for MXFP4 (layout above), ignored otherwise
  *   h   [rows_upper_bound, I] act dtype (written; intermediate)
  *   out [rows_upper_bound, D] act dtype (written)
- *   rows_upper_bound  host-known bound on offsets[n_groups]; it sizes the grid
+ *   rows_upper_bound  host-known bound on offsets[n_groups]; it sizes the grid;
+ *                     rows_upper_bound * max(D, I) below 2^31, else MOE_ERR_SHAPE
  *   ws / ws_bytes     scratch of at least moe_grouped_ffn_workspace_size bytes
  *   With act_quant the quantised copies of the A rows and of h (and their
  *   scales) live in the workspace; h is still written in bf16 (it is the

@@ -518,6 +518,10 @@ moe_status_t moe_grouped_ffn_workspace_size(const moe_problem_t* p, int32_t n_gr
   if (st != MOE_OK) return st;
   if (!bytes) return MOE_ERR_NULL;
   if (n_groups < 1 || n_groups > 1024 || rows_upper_bound < 0) return MOE_ERR_SHAPE;
+  // the A rows, h and out hold rows_upper_bound rows: the same element bound
+  // as the layer's T*k rows (the tiled GEMM's 32-bit byte offsets)
+  if (static_cast<int64_t>(rows_upper_bound) * std::max(p->D, p->I) >= (int64_t(1) << 31))
+    return MOE_ERR_SHAPE;
   const Plan pl = make_plan(p, static_cast<double>(rows_upper_bound) / n_groups);
   *bytes = ffn_layout(p, pl, n_groups, rows_upper_bound).total;
   return MOE_OK;

@@ -190,6 +190,21 @@ def test_null_and_workspace_errors(lib):
     assert lib.moe_debug_fp8_to_bf16(fake, fake, 7, None) == B.MOE_ERR_SHAPE
 
 
+def test_grouped_ffn_rows_bound(lib):
+    """rows_upper_bound * max(D, I) must stay below 2^31, whatever T and k say."""
+    p = B.make_problem(64, 8192, 8, 2, 2048, 0)
+    n = ctypes.c_size_t(0)
+    ok = (1 << 31) // 8192 - 1
+    assert lib.moe_grouped_ffn_workspace_size(ctypes.byref(p), 8, ok, ctypes.byref(n)) == B.MOE_OK
+    assert lib.moe_grouped_ffn_workspace_size(ctypes.byref(p), 8, ok + 1, ctypes.byref(n)) == B.MOE_ERR_SHAPE
+    fake = 4096
+    assert lib.moe_grouped_ffn(ctypes.byref(p), 8, ok + 1, fake, None, fake, fake, None, fake, None,
+                               fake, fake, fake, 1 << 40, None) == B.MOE_ERR_SHAPE
+    q = B.make_problem(64, 256, 8, 2, 16384, 0)
+    assert lib.moe_grouped_ffn_workspace_size(ctypes.byref(q), 8, (1 << 31) // 16384,
+                                              ctypes.byref(n)) == B.MOE_ERR_SHAPE
+
+
 def test_zero_tokens_is_ok_and_launches_nothing(lib):
     p = _ok_problem(T=0)
     need = B.moe_layer_workspace_size(p)
