@@ -214,7 +214,8 @@ moe_status_t moe_grouped_ffn(const moe_problem_t* p, int32_t n_groups, int32_t r
  *   y[t] = sum_{j<k} topk_w[t,j] * o_perm[row_of_slot[t*k+j]] + shared_out[t]
  *   accumulated in fp32 in slot order, rounded once to the act dtype.
  *   o_perm [T*k, D], shared_out [T, D] or NULL, y [T, D]: act dtype.
- *   Assignments with row_of_slot < 0 contribute nothing.
+ *   Assignments whose row_of_slot is negative or not below T*k contribute
+ *   nothing.
  */
 moe_status_t moe_combine(const moe_problem_t* p, const void* o_perm, const int32_t* row_of_slot,
                          const float* topk_w, const void* shared_out, void* y, void* stream);

@@ -75,7 +75,9 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const void* __restrict
   __shared__ float ws[MAXK];
   const int t = blockIdx.x;
   if (threadIdx.x < k) {
-    rows[threadIdx.x] = row_of_slot[static_cast<int64_t>(t) * k + threadIdx.x];
+    // rows outside [0, T*k) (the grid has T blocks in x) are dropped assignments
+    const int32_t r = row_of_slot[static_cast<int64_t>(t) * k + threadIdx.x];
+    rows[threadIdx.x] = (r >= 0 && r < static_cast<int64_t>(gridDim.x) * k) ? r : -1;
     ws[threadIdx.x] = w[static_cast<int64_t>(t) * k + threadIdx.x];
   }
   __syncthreads();

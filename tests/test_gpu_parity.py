@@ -278,6 +278,27 @@ def test_moe_combine_reproduces_gathered_rows():
     assert rel_err(y.cpu().numpy(), x.numpy()) < 1e-6
 
 
+def test_moe_combine_drops_rows_out_of_range():
+    """Assignments whose row is negative or not below T*k add nothing."""
+    T, k, D = 64, 3, 128
+    rng = np.random.default_rng(2)
+    o = torch.randn(T * k, D, dtype=torch.float32)
+    rows = rng.permutation(T * k).astype(np.int32).reshape(T, k)
+    rows[::3, 0] = -1
+    rows[1::3, 1] = T * k
+    rows[2::5, 2] = np.iinfo(np.int32).max
+    w = rng.random((T, k)).astype(np.float32)
+    sh = torch.randn(T, D, dtype=torch.float32)
+    p = B.make_problem(T, D, 8, k, 64, act_dtype="f32", w_dtype="f32")
+    y = torch.empty(T, D, device="cuda")
+    B.moe_combine(p, o.cuda(), torch.from_numpy(rows).cuda(), torch.from_numpy(w).cuda(), sh.cuda(), y)
+    torch.cuda.synchronize()
+    on = torch.from_numpy((rows >= 0) & (rows < T * k))
+    idx = torch.from_numpy(np.clip(rows, 0, T * k - 1).astype(np.int64))
+    ref = (o.double()[idx] * (torch.from_numpy(w).double() * on)[..., None]).sum(1) + sh.double()
+    assert torch.allclose(y.cpu().double(), ref, rtol=1e-5, atol=1e-5)
+
+
 @pytest.mark.parametrize("policy", ["stream", "lds", "auto"])
 @pytest.mark.parametrize("name", ["qwen_ragged", "ling_fp8", "gemma_like", "ling_decode_like",
                                   "qwen_decode_deep"])
