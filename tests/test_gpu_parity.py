@@ -119,6 +119,19 @@ def test_layer_edge_shapes(over):
     assert rel_err(f64(res["y"]), ref["y"]) <= tol_for(cfg)
 
 
+# The largest expert count and top-k the library takes (E = 1024, k = 32),
+# through the one-launch permutation (T <= 1024) and the multi-block one
+@pytest.mark.parametrize("T,policy", [(100, "auto"), (100, "lds"), (1100, "auto"), (1100, "lds")])
+def test_layer_max_experts_and_k(T, policy):
+    cfg = shrink(CONFIGS["qwen_decode"], T=T, D=128, E=1024, k=32, I=64, I_shared=64)
+    print(f"[max E and k] T={T} policy={policy}", flush=True)
+    wl = to_device(generate(cfg, seed=7))
+    ref = oracle_layer(wl)
+    res = run_layer(wl, policy, logits_in=torch.from_numpy(ref["logits"]).cuda())
+    _check_routing(res, ref)
+    assert rel_err(f64(res["y"]), ref["y"]) <= tol_for(cfg)
+
+
 # 256-row tiles with skewed loads: hot experts with two to four tiles next to
 # one-tile and empty experts, and one expert taking every token (16 tiles)
 @pytest.mark.parametrize("T,k,skew", [(2000, 2, 0.15), (4096, 1, None)])
