@@ -172,6 +172,12 @@ hipError_t launch_permute_small(const int32_t* idx, int T, int k, int E, int32_t
 hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int bm, int max_rows,
                               int max_tiles, bool largest_first, GTile* tiles, int32_t* n_tiles,
                               hipStream_t s);
+// Two tables of the same groups in the same order in one launch: bm-row tiles
+// (at most max_tiles) and bm2-row tiles (at most max_tiles2).
+hipError_t launch_build_tiles_pair(const int32_t* offsets, int n_groups, int max_rows,
+                                   bool largest_first, int bm, int max_tiles, GTile* tiles,
+                                   int32_t* n_tiles, int bm2, int max_tiles2, GTile* tiles2,
+                                   int32_t* n_tiles2, hipStream_t s);
 
 // Grouped GEMM, streamed weights.  mt = 16-row chunks per m-tile (1, 2, 4).
 // gated: h = act(A.Wg^T * sg) * (A.Wu^T * su); plain: out = A.W^T * s.

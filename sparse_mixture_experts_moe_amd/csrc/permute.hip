@@ -8,9 +8,10 @@
 //   1. each block of PB tokens sets, in LDS, one bit per (expert, token) pair;
 //      a token's rank inside its expert is the popcount of the bits of lower
 //      tokens, and the block's count is the popcount of the whole mask;
-//   2. one block scans the per-block counts down each expert column and then
-//      across experts (exclusive), giving every (block, expert) its base row;
-//   3. every assignment writes row = base + rank.
+//   2. one block scans the per-block counts down each expert column (each
+//      block's first row within the expert) and across experts (exclusive:
+//      the expert's first row, its offset);
+//   3. every assignment writes row = offset + the block's first row + rank.
 // Rows of one expert are therefore in ascending token order.
 #include "moe_kernels.h"
 
@@ -57,8 +58,9 @@ __global__ __launch_bounds__(PB) void perm_mask_kernel(const int32_t* __restrict
   }
 }
 
-// Single block: column scans of the per-block counts (turned into base rows in
-// place), counts, and the exclusive scan over experts.
+// Single block: column scans of the per-block counts (turned in place into
+// each block's first row within the expert), counts, and the exclusive scan
+// over experts (the scatter adds offsets[e]).
 __global__ __launch_bounds__(SCAN_THREADS) void perm_scan_kernel(int32_t* __restrict__ blk, int nb,
                                                                  int E, int32_t* __restrict__ counts,
                                                                  int32_t* __restrict__ offsets) {
@@ -66,10 +68,18 @@ __global__ __launch_bounds__(SCAN_THREADS) void perm_scan_kernel(int32_t* __rest
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) {
-      const int c = blk[static_cast<int64_t>(b) * E + e];
-      blk[static_cast<int64_t>(b) * E + e] = run;
-      run += c;
+    constexpr int NB = 16;   // counts loaded before any is replaced
+    for (int b0 = 0; b0 < nb; b0 += NB) {
+      int c[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        c[u] = b0 + u < nb ? blk[static_cast<int64_t>(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < NB; ++u)
+        if (b0 + u < nb) {
+          blk[static_cast<int64_t>(b0 + u) * E + e] = run;
+          run += c[u];
+        }
     }
     counts[e] = run;
   }
@@ -86,13 +96,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void perm_scan_kernel(int32_t* __rest
   if (e < E) {
     offsets[e] = excl;
     if (e == E - 1) offsets[E] = sc[e];
-    for (int b = 0; b < nb; ++b) blk[static_cast<int64_t>(b) * E + e] += excl;
   }
 }
 
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ idx,
                                                            const int32_t* __restrict__ local_rank,
-                                                           const int32_t* __restrict__ blk, int T,
+                                                           const int32_t* __restrict__ blk,
+                                                           const int32_t* __restrict__ offsets, int T,
                                                            int k, int E,
                                                            int32_t* __restrict__ row_token,
                                                            int32_t* __restrict__ row_of_slot) {
@@ -104,7 +114,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
     row_of_slot[a] = -1;
     return;
   }
-  const int r = blk[static_cast<int64_t>(t / PB) * E + e] + local_rank[a];
+  const int r = offsets[e] + blk[static_cast<int64_t>(t / PB) * E + e] + local_rank[a];
   row_token[r] = t;
   row_of_slot[a] = r;
 }
@@ -137,7 +147,8 @@ __device__ __forceinline__ int spread_rank(int g, int G) {
 
 // Single block: each group's M-tiles.  With largest_first the groups are
 // ordered by descending row count (ties by group id) so the heaviest experts
-// start first; otherwise in group order.
+// start first; otherwise in group order.  With tiles2, a second table of
+// bm2-row tiles in the same group order (one ranking, one scan for both).
 constexpr int TILE_THREADS = 1024;
 
 __device__ __forceinline__ int clamp_row(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -146,9 +157,13 @@ __global__ __launch_bounds__(TILE_THREADS) void build_tiles_kernel(const int32_t
                                                                    int G, int bm, int max_rows,
                                                                    int max_tiles, int largest_first,
                                                                    GTile* __restrict__ tiles,
-                                                                   int32_t* __restrict__ n_tiles) {
+                                                                   int32_t* __restrict__ n_tiles, int bm2,
+                                                                   int max_tiles2,
+                                                                   GTile* __restrict__ tiles2,
+                                                                   int32_t* __restrict__ n_tiles2) {
   __shared__ int32_t sz[TILE_THREADS];    // group sizes (offsets clamped to [0, max_rows])
   __shared__ int32_t ntl[TILE_THREADS];   // tiles of the group at each rank position
+  __shared__ int32_t ntl2[TILE_THREADS];  // the same for the second table
   __shared__ int32_t grp[TILE_THREADS];   // group at each rank position
   const int g = threadIdx.x;
   int r0 = 0, n = 0;
@@ -170,37 +185,50 @@ __global__ __launch_bounds__(TILE_THREADS) void build_tiles_kernel(const int32_t
     }
 #endif
   }
+  const bool two = tiles2 != nullptr;
   ntl[g] = 0;
+  ntl2[g] = 0;
   __syncthreads();
   if (g < G) {
     ntl[rank] = (n + bm - 1) / bm;
+    if (two) ntl2[rank] = (n + bm2 - 1) / bm2;
     grp[rank] = g;
   }
   __syncthreads();
-  // inclusive scan of tile counts in rank order
+  // inclusive scans of tile counts in rank order
   for (int off = 1; off < TILE_THREADS; off <<= 1) {
     const int add = g >= off ? ntl[g - off] : 0;
+    const int add2 = g >= off ? ntl2[g - off] : 0;
     __syncthreads();
     ntl[g] += add;
+    ntl2[g] += add2;
     __syncthreads();
   }
-  if (g < G) {
+  auto write = [&](GTile* tl_out, const int32_t* sc, int tb, int cap) {
     const int gg = grp[g];
     const int a = clamp_row(offsets[gg], 0, max_rows);
     const int b = a + sz[gg];
-    const int base = g > 0 ? ntl[g - 1] : 0;
-    for (int i = 0, r = a; r < b && base + i < max_tiles; ++i, r += bm) {
+    const int base = g > 0 ? sc[g - 1] : 0;
+    for (int i = 0, r = a; r < b && base + i < cap; ++i, r += tb) {
       GTile tl;
       tl.group = gg;
       tl.row0 = r;
-      tl.row1 = r + bm < b ? r + bm : b;
+      tl.row1 = r + tb < b ? r + tb : b;
       tl.pad = 0;
-      tiles[base + i] = tl;
+      tl_out[base + i] = tl;
     }
+  };
+  if (g < G) {
+    write(tiles, ntl, bm, max_tiles);
+    if (two) write(tiles2, ntl2, bm2, max_tiles2);
   }
   if (g == 0) {
     const int total = G > 0 ? ntl[G - 1] : 0;
     n_tiles[0] = total < max_tiles ? total : max_tiles;
+    if (two) {
+      const int total2 = G > 0 ? ntl2[G - 1] : 0;
+      n_tiles2[0] = total2 < max_tiles2 ? total2 : max_tiles2;
+    }
   }
 }
 
@@ -348,7 +376,7 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* blk,
   const int64_t n = static_cast<int64_t>(T) * k;
   if (n > 0) {
     perm_scatter_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
-        idx, local_rank, blk, T, k, E, row_token, row_of_slot);
+        idx, local_rank, blk, offsets, T, k, E, row_token, row_of_slot);
   }
   return hipGetLastError();
 }
@@ -357,7 +385,19 @@ hipError_t launch_build_tiles(const int32_t* offsets, int n_groups, int bm, int 
                               int max_tiles, bool largest_first, GTile* tiles, int32_t* n_tiles,
                               hipStream_t s) {
   build_tiles_kernel<<<1, TILE_THREADS, 0, s>>>(offsets, n_groups, bm, max_rows, max_tiles,
-                                                largest_first ? 1 : 0, tiles, n_tiles);
+                                                largest_first ? 1 : 0, tiles, n_tiles, 0, 0, nullptr,
+                                                nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_tiles_pair(const int32_t* offsets, int n_groups, int max_rows,
+                                   bool largest_first, int bm, int max_tiles, GTile* tiles,
+                                   int32_t* n_tiles, int bm2, int max_tiles2, GTile* tiles2,
+                                   int32_t* n_tiles2, hipStream_t s) {
+  if (!tiles2 || bm2 <= 0) return hipErrorInvalidValue;
+  build_tiles_kernel<<<1, TILE_THREADS, 0, s>>>(offsets, n_groups, bm, max_rows, max_tiles,
+                                                largest_first ? 1 : 0, tiles, n_tiles, bm2,
+                                                max_tiles2, tiles2, n_tiles2);
   return hipGetLastError();
 }
 

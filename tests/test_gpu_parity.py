@@ -33,6 +33,12 @@ SMALL = {
     # bf16 decode with K = D = 2304 on the gate/up projection: the 32-row
     # shape's 256-deep stages (9 of them), 128-deep ones on the down projection
     "qwen_decode_deep": shrink(CONFIGS["qwen_decode"], T=40, D=2304, E=32, k=6, I=384, I_shared=128),
+    # about 150 rows per expert with D = 512: 256-row tiles for gate/up, the
+    # down projection on 128 x 512 tiles from a tile table of its own
+    "qwen_prefill_like": shrink(CONFIGS["qwen_prefill"], T=600, D=512, E=32, k=8, I=128, I_shared=128),
+    # bf16 routed experts with an fp8 shared expert: one launch per weight dtype
+    "mixed_dtypes": shrink(CONFIGS["qwen_prefill"], T=600, D=512, E=32, k=8, I=128, I_shared=128,
+                           shared_w_dtype="fp8"),
 }
 
 
