@@ -14,6 +14,11 @@ namespace {
 constexpr int THREADS = 128;
 constexpr int CHUNK = THREADS * 8;   // hidden elements per block
 constexpr int MAXK = 32;
+// Block order: 1 = a token's column chunks in consecutive blocks (the blocks
+// in flight read whole expert rows), 0 = chunk-major (token index fastest).
+#ifndef MOE_COMBINE_ROWMAJOR
+#define MOE_COMBINE_ROWMAJOR 1
+#endif
 
 // 8 elements as stored (bf16: 16 bytes; fp32: 32 bytes), loaded without use
 // so that several rows' loads can be in flight together
@@ -69,20 +74,27 @@ template <int DT>
 __global__ __launch_bounds__(THREADS) void combine_kernel(const void* __restrict__ o_perm,
                                                           const int32_t* __restrict__ row_of_slot,
                                                           const float* __restrict__ w,
-                                                          const void* __restrict__ shared, int D,
-                                                          int k, void* __restrict__ y) {
+                                                          const void* __restrict__ shared, int T,
+                                                          int D, int k, void* __restrict__ y) {
   __shared__ int32_t rows[MAXK];
   __shared__ float ws[MAXK];
+#if MOE_COMBINE_ROWMAJOR
+  const int nch = (D + CHUNK - 1) / CHUNK;
+  const int t = static_cast<int>(blockIdx.x / nch);
+  const int chunk = static_cast<int>(blockIdx.x - static_cast<unsigned>(t) * nch);
+#else
   const int t = blockIdx.x;
+  const int chunk = blockIdx.y;
+#endif
   if (threadIdx.x < k) {
-    // rows outside [0, T*k) (the grid has T blocks in x) are dropped assignments
+    // rows outside [0, T*k) are dropped assignments
     const int32_t r = row_of_slot[static_cast<int64_t>(t) * k + threadIdx.x];
-    rows[threadIdx.x] = (r >= 0 && r < static_cast<int64_t>(gridDim.x) * k) ? r : -1;
+    rows[threadIdx.x] = (r >= 0 && r < static_cast<int64_t>(T) * k) ? r : -1;
     ws[threadIdx.x] = w[static_cast<int64_t>(t) * k + threadIdx.x];
   }
   __syncthreads();
   {
-    const int d = blockIdx.y * CHUNK + threadIdx.x * 8;
+    const int d = chunk * CHUNK + threadIdx.x * 8;
     if (d >= D) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     Raw8<DT> sraw;
@@ -126,11 +138,16 @@ hipError_t launch_combine(const void* o_perm, const int32_t* row_of_slot, const 
                           const void* shared, int T, int D, int k, int dtype, void* y,
                           hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const dim3 grid(T, (D + CHUNK - 1) / CHUNK);
+  const int nch = (D + CHUNK - 1) / CHUNK;
+#if MOE_COMBINE_ROWMAJOR
+  const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(T) * nch));   // T * D < 2^31
+#else
+  const dim3 grid(T, nch);
+#endif
   if (dtype == DT_BF16)
-    combine_kernel<DT_BF16><<<grid, THREADS, 0, s>>>(o_perm, row_of_slot, w, shared, D, k, y);
+    combine_kernel<DT_BF16><<<grid, THREADS, 0, s>>>(o_perm, row_of_slot, w, shared, T, D, k, y);
   else
-    combine_kernel<DT_F32><<<grid, THREADS, 0, s>>>(o_perm, row_of_slot, w, shared, D, k, y);
+    combine_kernel<DT_F32><<<grid, THREADS, 0, s>>>(o_perm, row_of_slot, w, shared, T, D, k, y);
   return hipGetLastError();
 }
 
