@@ -18,40 +18,12 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-// One block per token.  The router product may arrive as `splits` partial sums
-// (a K-split GEMM): all threads of the block add them in slice order into LDS
-// (so the logits are deterministic), then wavefront 0 selects the top k.
-// Blocks are 256 threads when there are partial sums to add, else one wavefront.
-template <int EPL, int TOPK_THREADS>
-__global__ __launch_bounds__(TOPK_THREADS) void topk_softmax_kernel(
-    const float* __restrict__ part, int splits, float* __restrict__ logits_out, int T, int E,
-    int k, int renorm, int32_t* __restrict__ idx, float* __restrict__ wout) {
-  __shared__ float lg[64 * EPL];
-  const int t = blockIdx.x;
-  const int64_t slice = static_cast<int64_t>(T) * E;
-  const float* row = part + static_cast<int64_t>(t) * E;
-  for (int e = threadIdx.x; e < E; e += TOPK_THREADS) {
-    float l = row[e];
-    for (int s0 = 1; s0 < splits; s0 += 8) {
-      float pv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) pv[u] = s0 + u < splits ? row[(s0 + u) * slice + e] : 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (s0 + u < splits) l += pv[u];
-    }
-    lg[e] = l;
-    if (logits_out) logits_out[static_cast<int64_t>(t) * E + e] = l;
-  }
-  __syncthreads();
-  if (threadIdx.x >= 64) return;
-  const int lane = threadIdx.x;
-  float v[EPL];
-#pragma unroll
-  for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    v[j] = e < E ? lg[e] : -__builtin_inff();
-  }
+// k rounds of a wavefront arg-max over the lane's EPL logits v (expert
+// lane + 64 j), then the weights; lane r < k stores slot r of token t.
+template <int EPL>
+__device__ __forceinline__ void select_topk(const float (&v)[EPL], int lane, int t, int E, int k,
+                                            int renorm, int32_t* __restrict__ idx,
+                                            float* __restrict__ wout) {
   uint32_t taken = 0;
   float my_v = 0.f, top_v = 0.f;
   int my_i = 0;
@@ -102,11 +74,95 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_softmax_kernel(
   }
 }
 
-template <int EPL, int THREADS>
+
+// One block per token.  The router product may arrive as `splits` partial sums
+// (a K-split GEMM): all threads of the block add them in slice order into LDS
+// (so the logits are deterministic), then wavefront 0 selects the top k.
+// Used for many partial sums (a decode batch's router).
+template <int EPL, int TOPK_THREADS>
+__global__ __launch_bounds__(TOPK_THREADS) void topk_softmax_kernel(
+    const float* __restrict__ part, int splits, float* __restrict__ logits_out, int T, int E,
+    int k, int renorm, int32_t* __restrict__ idx, float* __restrict__ wout) {
+  __shared__ float lg[64 * EPL];
+  const int t = blockIdx.x;
+  const int64_t slice = static_cast<int64_t>(T) * E;
+  const float* row = part + static_cast<int64_t>(t) * E;
+  for (int e = threadIdx.x; e < E; e += TOPK_THREADS) {
+    float l = row[e];
+    for (int s0 = 1; s0 < splits; s0 += 8) {
+      float pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pv[u] = s0 + u < splits ? row[(s0 + u) * slice + e] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < splits) l += pv[u];
+    }
+    lg[e] = l;
+    if (logits_out) logits_out[static_cast<int64_t>(t) * E + e] = l;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  float v[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? lg[e] : -__builtin_inff();
+  }
+  select_topk<EPL>(v, lane, t, E, k, renorm, idx, wout);
+}
+
+// Few partial sums (at most MOE_TOPK_WAVE_SPLITS): one wavefront per token,
+// four tokens per block, each lane adding its experts' partial sums in slice
+// order (the same additions as above), so every wavefront selects at once.
+#ifndef MOE_TOPK_WAVE_SPLITS
+#define MOE_TOPK_WAVE_SPLITS 4
+#endif
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_softmax_wave_kernel(
+    const float* __restrict__ part, int splits, float* __restrict__ logits_out, int T, int E,
+    int k, int renorm, int32_t* __restrict__ idx, float* __restrict__ wout) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int lane = threadIdx.x & 63;
+  const int64_t slice = static_cast<int64_t>(T) * E;
+  const float* row = part + static_cast<int64_t>(t) * E;
+  float v[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    v[j] = e < E ? row[e] : -__builtin_inff();
+  }
+  for (int s0 = 1; s0 < splits; ++s0) {
+    float pv[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      pv[j] = e < E ? row[s0 * slice + e] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + 64 * j < E) v[j] += pv[j];
+  }
+  if (logits_out) {
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) logits_out[static_cast<int64_t>(t) * E + e] = v[j];
+    }
+  }
+  select_topk<EPL>(v, lane, t, E, k, renorm, idx, wout);
+}
+
+template <int EPL>
 void go(const float* part, int splits, float* logits_out, int T, int E, int k, int renorm,
         int32_t* idx, float* w, hipStream_t s) {
-  topk_softmax_kernel<EPL, THREADS><<<T, THREADS, 0, s>>>(part, splits, logits_out, T, E, k,
-                                                          renorm, idx, w);
+  if (splits <= MOE_TOPK_WAVE_SPLITS)
+    topk_softmax_wave_kernel<EPL><<<(T + 3) / 4, 256, 0, s>>>(part, splits, logits_out, T, E, k,
+                                                              renorm, idx, w);
+  else
+    topk_softmax_kernel<EPL, 256><<<T, 256, 0, s>>>(part, splits, logits_out, T, E, k, renorm,
+                                                    idx, w);
 }
 
 }  // namespace
@@ -115,19 +171,11 @@ hipError_t launch_topk_softmax(const float* part, int splits, float* logits_out,
                                int k, int renorm, int32_t* idx, float* w, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int epl = (E + 63) / 64;
-  if (splits > 1) {
-    if (epl <= 1) go<1, 256>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
-    else if (epl <= 2) go<2, 256>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
-    else if (epl <= 4) go<4, 256>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
-    else if (epl <= 8) go<8, 256>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
-    else go<16, 256>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
-  } else {
-    if (epl <= 1) go<1, 64>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
-    else if (epl <= 2) go<2, 64>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
-    else if (epl <= 4) go<4, 64>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
-    else if (epl <= 8) go<8, 64>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
-    else go<16, 64>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
-  }
+  if (epl <= 1) go<1>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+  else if (epl <= 2) go<2>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+  else if (epl <= 4) go<4>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+  else if (epl <= 8) go<8>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
+  else go<16>(part, splits, logits_out, T, E, k, renorm, idx, w, s);
   return hipGetLastError();
 }
 
