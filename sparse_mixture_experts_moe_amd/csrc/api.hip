@@ -273,11 +273,12 @@ int router_splits(const moe_problem_t* p, const Plan& pl) {
   const int64_t m_tiles = (p->T + pl.bm - 1) / pl.bm;
   const int64_t items = pl.tiled ? m_tiles * tiled_blocks_n(TILED_NARROW, false, p->E)
                                  : m_tiles * stream_waves_n(false, p->E);
-  int s = 1;
+  // the most slices (a divisor of K / 64) that keeps each slice at least
+  // MOE_ROUTER_SLICE long and the work items at most MOE_ROUTER_ITEMS
   const int K = p->D;
-  while (K % (2 * s) == 0 && (K / (2 * s)) % 64 == 0 && K / (2 * s) >= MOE_ROUTER_SLICE &&
-         items * s < MOE_ROUTER_ITEMS)
-    s *= 2;
+  int s = 1;
+  for (int c = 2; c <= K / 64; ++c)
+    if ((K / 64) % c == 0 && K / c >= MOE_ROUTER_SLICE && items * c <= MOE_ROUTER_ITEMS) s = c;
   return s;
 }
 
