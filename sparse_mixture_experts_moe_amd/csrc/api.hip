@@ -251,8 +251,12 @@ void finish_grid(GArgs& g, const Plan& pl, bool gated) {
 // (decode): streamed GEMM with the K dimension split into slices whose fp32
 // partial sums the top-k kernel adds in slice order, so enough wavefronts
 // stream the router weight.
+#ifndef MOE_ROUTER_TILED_T      // tokens from which the router runs on the LDS-tiled GEMM
+#define MOE_ROUTER_TILED_T 512
+#endif
 Plan router_plan(const moe_problem_t* p) {
-  if (kTiledReady && p->act_dtype == MOE_BF16 && p->T >= 1024 && p->tile_policy != MOE_TILE_STREAM &&
+  if (kTiledReady && p->act_dtype == MOE_BF16 && p->T >= MOE_ROUTER_TILED_T &&
+      p->tile_policy != MOE_TILE_STREAM &&
       p->D % tiled_k_multiple() == 0 && tiled_offsets_fit(p->T, p->D, p->E, p->D, p->act_dtype))
     return Plan{true, 0, tiled_bm(TILED_WIDE), -1};
   int mt = p->T <= 16 ? 1 : p->T <= 32 ? 2 : 4;
