@@ -137,7 +137,8 @@ def rows_w8a8(tokens, x: np.ndarray, idx: np.ndarray, w: np.ndarray, expert,
     for n, t in enumerate(tokens):
         for j in range(k):
             by_e.setdefault(int(idx[t, j]), []).append((n, t, j))
-    for e, items in by_e.items():
+    for e in sorted(by_e):
+        items = by_e[e]
         w13, s13, w2, s2 = expert(e)
         o = expert_ffn_w8a8(xd[[n for n, _, _ in items]], w13, s13, w2, s2, act)
         for (n, t, j), orow in zip(items, o):

@@ -210,23 +210,28 @@ def layer_tokens(tokens, x: np.ndarray, idx: np.ndarray, w: np.ndarray,
                  act: str = "silu", act_shared: str = "silu") -> np.ndarray:
     """y for a subset of tokens, given their routing (idx, w rows for all T).
 
-    Evaluates step 6 token by token from the definition, so a large layer can be
-    checked on sampled outputs without running every expert.
+    Evaluates step 6 from the definition for the selected tokens only: every
+    (token, slot) assignment's expert FFN on that token's row, weighted and
+    summed, plus the shared branch.  Experts are visited in ascending id, each
+    once, over all selected rows routed to it, so one decoded expert is held at
+    a time.
     """
     x = np.asarray(x, np.float64)
     tokens = list(tokens)
     y = np.zeros((len(tokens), x.shape[1]), dtype=np.float64)
-    cache = {}
+    by_e = {}
     for n, t in enumerate(tokens):
         for j in range(idx.shape[1]):
-            e = int(idx[t, j])
-            if e not in cache:
-                cache[e] = expert(e)
-            w13, s13, w2, s2 = cache[e]
-            y[n] += float(w[t, j]) * expert_ffn(x[t:t + 1], w13, s13, w2, s2, act)[0]
-        if shared is not None:
-            w13s, s13s, w2s, s2s = shared
-            y[n] += expert_ffn(x[t:t + 1], w13s, s13s, w2s, s2s, act_shared)[0]
+            by_e.setdefault(int(idx[t, j]), []).append((n, t, j))
+    for e in sorted(by_e):
+        items = by_e[e]
+        w13, s13, w2, s2 = expert(e)
+        o = expert_ffn(x[[t for _, t, _ in items]], w13, s13, w2, s2, act)
+        for (n, t, j), orow in zip(items, o):
+            y[n] += float(w[t, j]) * orow
+    if shared is not None:
+        w13s, s13s, w2s, s2s = shared
+        y += expert_ffn(x[tokens], w13s, s13s, w2s, s2s, act_shared)
     return y
 
 
