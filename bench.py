@@ -26,7 +26,10 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-DEFAULT_WORKLOAD = "qwen_decode"
+# The largest configuration that fits one GPU and the one the prefill MFMA
+# target is quoted on: the Ling-2.6-1T-style layer at 16384 tokens, fp8
+# per-channel expert weights with bf16 activations (W8A16).
+DEFAULT_WORKLOAD = "ling_prefill"
 METRIC = "MoE-layer tokens/s; grouped-GEMM MFMA % of peak (prefill), HBM % (decode)"
 
 
@@ -53,6 +56,7 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
                     help="only run 10 plain device copies of MIB MiB (counter calibration)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the measured HBM / MFMA ceilings")
     return ap.parse_args()
 
 
@@ -69,6 +73,61 @@ def copy_calib(mib: int):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calib_bytes": n, "copies": 10}), flush=True)
+
+
+def cpu_identity():
+    """(CPU model, number of cores this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
+def measured_peaks(B, stream):
+    """The GPU's own ceilings, measured in this job with the library's probes:
+    a streaming read of 4 GiB, and register-only bf16 and fp8 MFMA loops on
+    random operands (each launch about 20 ms; median of 5 after 2 warm-ups)."""
+    import torch
+
+    def timed(fn, reps=5, warm=2):
+        for _ in range(warm):
+            fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return sorted(ts)[len(ts) // 2]
+
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    t = timed(lambda: B.moe_probe_hbm_read(buf, nbytes, sink, stream))
+    hbm = nbytes / t / 1e9
+    del buf
+    g = torch.Generator().manual_seed(0)
+    ops = torch.randn(65536, generator=g)
+    fs = torch.empty(B.moe_probe_mfma_sink_floats(), dtype=torch.float32, device="cuda")
+    out = {"hbm_read_GBps": hbm}
+    for dt, o, iters in (("bf16", ops[:32768].to(torch.bfloat16), 37000),
+                         ("fp8", ops.to(torch.float8_e4m3fn), 18600)):
+        od = o.view(torch.uint8).cuda()
+        flop = [0.0]
+
+        def run():
+            flop[0] = B.moe_probe_mfma(dt, od, iters, fs, stream)
+        t = timed(run)
+        out[f"mfma_{dt}_TFLOPs"] = flop[0] / t / 1e12
+    return out
 
 
 MIN_CPU_S, MAX_CPU_S = 10.0, 30.0   # CPU baseline: seconds of oracle work
@@ -127,7 +186,9 @@ def cpu_baseline(wl, n_tokens: int, act_quant: int = 0):
     for info in threadpool_info():
         if info.get("user_api") == "blas":
             threads = max(threads, int(info.get("num_threads", 1)))
+    model, affinity = cpu_identity()
     return {"value": passes * n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "cpus_available": affinity,
             "sample": (f"float64 NumPy oracle{['', ' (W8A8)', ' (W4A8)'][act_quant]}, whole layer on the "
                        f"first {n_tokens} of {c.T} tokens "
                        f"({len(used)} experts decoded from {c.w_dtype} in each pass), "
@@ -242,6 +303,11 @@ def main():
                 "peak": cm.PEAK_TFLOPS[wdt], "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
+    peaks = None if args.no_peaks else measured_peaks(B, stream)
+    if peaks:
+        m = peaks["hbm_read_GBps"] if roof["bound"] == "hbm" else peaks[f"mfma_{wdt}_TFLOPs"]
+        roof["measured_peak"] = m
+        roof["frac_of_measured"] = roof["achieved"] / m
     roof.update({"kernel": name, "avg_launch_ms": avg_ms, "algorithmic_bytes": bytes_,
                  "algorithmic_flops": flops})
 
@@ -263,10 +329,13 @@ def main():
             "hbm_frac_layer_bytes": cm.layer_bytes(cfg, touched) / (ms_per_step * 1e-3)
             / (cm.PEAK_HBM_GBS * 1e9)},
         "stages_ms_per_step": {k: v[0] / diag_steps for k, v in diag.items()},
+        "measured_peaks": peaks,
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:
-        n = args.cpu_sample_tokens or {"qwen_decode": 64, "ling_decode": 16}.get(cfg.name, 16)
+        # a sample of about 10-30 s of oracle work on the host
+        n = args.cpu_sample_tokens or {"qwen_decode": 64, "ling_decode": 16, "ling_prefill": 4,
+                                       "ling_prefill_mxfp4": 4}.get(cfg.name, 16)
         out["cpu_baseline"] = cpu_baseline(wl, min(n, cfg.T), aq)
     print(json.dumps(out), flush=True)
 

@@ -19,7 +19,9 @@
  *  - The caller owns every buffer.  The library never allocates or frees
  *    device memory and keeps no per-call state, so calls on different streams
  *    are independent as long as their output and workspace buffers are
- *    disjoint.
+ *    disjoint.  The one piece of library state is the optional stage timing
+ *    record (moe_timing_enable / moe_timing_read), which belongs to the host
+ *    thread that enables it.
  *  - Errors are return values (moe_status_t).  Nothing throws, aborts or
  *    prints.  Validation is synchronous and happens before anything is
  *    enqueued; a failed launch returns MOE_ERR_LAUNCH.
@@ -156,23 +158,31 @@ moe_status_t moe_route(const moe_problem_t* p, const void* x, const void* w_rout
 /*
  * moe_permute -- per-expert token counts and the stable expert-major
  * permutation ("init routing" and "compute expert tokens" on the CANN
- * Qwen3-MoE page; the contiguous permuted buffer of the SparseCore gather on
- * the Ironwood page, MoE track).
+ * Qwen3-MoE page), and optionally the contiguous permuted copy of the tokens
+ * (the gather into one buffer of the SparseCore path on the Ironwood page, MoE
+ * track).
  *   topk_idx    [T, k] int32, each row k distinct ids in [0, E)
  *   counts      [E]    rows routed to each expert
  *   offsets     [E+1]  exclusive prefix sum of counts (offsets[E] = T*k)
  *   row_token   [T*k]  token of each sorted row; rows of one expert are in
  *                      ascending token order
  *   row_of_slot [T*k]  sorted row of assignment (t, j) at index t*k + j
+ *   x, x_perm          both NULL, or both given: x [T, D] act dtype and
+ *                      x_perm [T*k, D] act dtype, 16-byte aligned; then
+ *                      x_perm[r] = x[row_token[r]] for r < offsets[E] (rows
+ *                      past it are not written).  moe_grouped_ffn can read
+ *                      x_perm directly (row_token = NULL); the fused layer
+ *                      gathers inside its GEMM instead and never builds it.
  *   ws / ws_bytes      scratch of at least moe_permute_workspace_size bytes
  * Deterministic: no order-dependent atomics.  Ids outside [0, E) are a
  * caller error: they are dropped (row_of_slot = -1) and counts then sum to
- * less than T*k; repeated ids within a row are a caller error too.
+ * less than T*k; repeated ids within a row are a caller error too.  Exactly
+ * one of x / x_perm NULL is MOE_ERR_NULL; a misaligned one MOE_ERR_SHAPE.
  */
 moe_status_t moe_permute_workspace_size(const moe_problem_t* p, size_t* bytes);
 moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
-                         int32_t* offsets, int32_t* row_token, int32_t* row_of_slot,
-                         void* ws, size_t ws_bytes, void* stream);
+                         int32_t* offsets, int32_t* row_token, int32_t* row_of_slot, const void* x,
+                         void* x_perm, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_grouped_ffn -- grouped gated expert FFN over n_groups experts.
@@ -304,12 +314,36 @@ const char* moe_status_string(moe_status_t status);
  * the other stages).  moe_timing_read waits for the recorded events, adds each stage's
  * elapsed time (ms) and launch count into ms[stage] / launches[stage] for
  * stage < n_stages, and clears the record.  Stage names: moe_stage_name.
- * Not thread-safe; meant for a single benchmarking thread.
+ * The record (enable flag, stage mask, pending events) is per host thread:
+ * enabling timing on one thread does not time calls made on another, and
+ * moe_timing_read returns the calling thread's stages only.
  */
 moe_status_t moe_timing_enable(int32_t on);
 moe_status_t moe_timing_read(double* ms, int32_t* launches, int32_t n_stages);
 int32_t moe_stage_count(void);
 const char* moe_stage_name(int32_t stage);
+
+/*
+ * Measurement probes (not part of the layer): the ceilings the benchmark
+ * reports next to the published peaks, measured on the part it runs on.
+ *  moe_probe_hbm_read   streams `bytes` (a multiple of 16, buf 16-byte
+ *                       aligned) from buf with eight 16-byte non-temporal
+ *                       loads in flight per thread; sink [1024] uint32 is
+ *                       written only if a data-dependent fold hits a magic
+ *                       value (it exists so the loads cannot be dropped).
+ *  moe_probe_mfma       independent register-only MFMAs, iters rounds per
+ *                       wavefront, on operands read from 64 KiB at `operands`
+ *                       (finite values of the probe's type: bf16 for MOE_BF16,
+ *                       the bf16 GEMMs' 16x16x32 instruction; e4m3fn codes for
+ *                       MOE_FP8_E4M3FN, the fp8 x fp8 GEMM's 32x32x64 one);
+ *                       *flop (host) receives the launch's FLOP count; sink
+ *                       holds moe_probe_mfma_sink_floats() floats.
+ * Time them with events on `stream`.
+ */
+moe_status_t moe_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+int32_t moe_probe_mfma_sink_floats(void);
+moe_status_t moe_probe_mfma(int32_t dtype, const void* operands, int32_t iters, float* sink,
+                            double* flop, void* stream);
 
 /*
  * Diagnostic: decode n (a multiple of 8) fp8 e4m3fn codes to bf16 bit

@@ -57,7 +57,8 @@ _LIB = None
 _SIG = {
     "moe_route": [ctypes.POINTER(MoeProblem), _vp, _vp, _vp, ctypes.c_int32, _vp, _vp, _vp],
     "moe_permute_workspace_size": [ctypes.POINTER(MoeProblem), ctypes.POINTER(ctypes.c_size_t)],
-    "moe_permute": [ctypes.POINTER(MoeProblem), _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
+    "moe_permute": [ctypes.POINTER(MoeProblem), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
+                    _vp],
     "moe_grouped_ffn_workspace_size": [ctypes.POINTER(MoeProblem), ctypes.c_int32, ctypes.c_int32,
                                        ctypes.POINTER(ctypes.c_size_t)],
     "moe_grouped_ffn": [ctypes.POINTER(MoeProblem), ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp,
@@ -71,6 +72,9 @@ _SIG = {
     "moe_stage_count": [],
     "moe_stage_name": [ctypes.c_int32],
     "moe_debug_fp8_to_bf16": [_vp, _vp, ctypes.c_int32, _vp],
+    "moe_probe_hbm_read": [_vp, ctypes.c_int64, _vp, _vp],
+    "moe_probe_mfma_sink_floats": [],
+    "moe_probe_mfma": [ctypes.c_int32, _vp, ctypes.c_int32, _vp, ctypes.POINTER(ctypes.c_double), _vp],
     "moe_quantize_rows": [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _vp, _vp, _vp],
     "moe_quantize_rows_mx": [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _vp, _vp, _vp],
 }
@@ -144,9 +148,10 @@ def moe_permute_workspace_size(p: MoeProblem) -> int:
 
 
 def moe_permute(p: MoeProblem, topk_idx, counts, offsets, row_token, row_of_slot, ws, ws_bytes,
-                stream=None):
+                stream=None, x=None, x_perm=None):
     _check(lib().moe_permute(ctypes.byref(p), _p(topk_idx), _p(counts), _p(offsets), _p(row_token),
-                             _p(row_of_slot), _p(ws), ws_bytes, _stream(stream)), "moe_permute")
+                             _p(row_of_slot), _p(x), _p(x_perm), _p(ws), ws_bytes, _stream(stream)),
+           "moe_permute")
 
 
 def moe_grouped_ffn_workspace_size(p: MoeProblem, n_groups: int, rows_upper_bound: int) -> int:
@@ -226,6 +231,22 @@ def moe_quantize_rows(a, rows: int, cols: int, lda: int, q, scale, stream=None):
 def moe_quantize_rows_mx(a, rows: int, cols: int, lda: int, q, scale, stream=None):
     _check(lib().moe_quantize_rows_mx(_p(a), rows, cols, lda, _p(q), _p(scale), _stream(stream)),
            "moe_quantize_rows_mx")
+
+
+def moe_probe_hbm_read(buf, nbytes: int, sink, stream=None):
+    _check(lib().moe_probe_hbm_read(_p(buf), nbytes, _p(sink), _stream(stream)), "moe_probe_hbm_read")
+
+
+def moe_probe_mfma_sink_floats() -> int:
+    return lib().moe_probe_mfma_sink_floats()
+
+
+def moe_probe_mfma(dtype: str, operands, iters: int, sink, stream=None) -> float:
+    """Launches the MFMA probe; returns the launch's FLOP count."""
+    flop = ctypes.c_double(0.0)
+    _check(lib().moe_probe_mfma(DTYPES[dtype], _p(operands), iters, _p(sink), ctypes.byref(flop),
+                                _stream(stream)), "moe_probe_mfma")
+    return flop.value
 
 
 def moe_debug_fp8_to_bf16(codes, out, n: int, stream=None):

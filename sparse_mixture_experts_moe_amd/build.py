@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 
 SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn_stream.hip", "ffn_tiled.hip", "actquant.hip",
-           "combine.hip"]
+           "combine.hip", "probe.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

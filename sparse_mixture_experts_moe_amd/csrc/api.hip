@@ -123,39 +123,19 @@ struct Plan {
 
 constexpr bool kTiledReady = true;
 
-// Largest mean rows per group for which the streamed GEMM uses 16-row /
-// 32-row tiles (build-time tuning knobs).
-#ifndef MOE_MT1_MEAN
-#define MOE_MT1_MEAN 4.0
-#endif
-#ifndef MOE_MT2_MEAN
-#define MOE_MT2_MEAN 24.0
-#endif
-// Tiled GEMM block order: 1 = N block by N block (an expert's tiles that read
-// the same weight slab run back to back), 0 = tile by tile.
-#ifndef MOE_TILED_NMAJOR
-#define MOE_TILED_NMAJOR 0
-#endif
-// Largest mean rows per group for which the tiled GEMM uses 256-row tiles.
-#ifndef MOE_TALL_MEAN
-#define MOE_TALL_MEAN 192.0
-#endif
-// fp8 weights: groups averaging more than MOE_SMALL_MIN and at most
-// MOE_SMALL_MAX rows run on the tiled GEMM's 32-row shape (0 = off).
-#ifndef MOE_TILED_SMALL
-#define MOE_TILED_SMALL 1
-#endif
-#ifndef MOE_SMALL_MIN
-#define MOE_SMALL_MIN 8.0
-#endif
-#ifndef MOE_SMALL_MAX
-#define MOE_SMALL_MAX 48.0
-#endif
-// bf16 weights on the 32-row shape too, below MOE_SMALL_MAX rows per group
-#ifndef MOE_SMALL_BF16
-#define MOE_SMALL_BF16 1
-#endif
-
+// Tile policy thresholds on the mean rows per group (the measured choices):
+//  - streamed GEMM: 16-row tiles up to kStream16Mean, 32-row up to
+//    kStream32Mean, 64-row beyond;
+//  - LDS-tiled GEMM: the 32-row shape for decode-sized groups (up to
+//    kSmallMax; fp8 weights above kSmallMin, since below it the streamed
+//    kernel's 16-row tiles read fewer padded rows), 256-row tiles up to
+//    kTallMean (an expert's weights are read once per 256 rows), 128-row
+//    tiles beyond.
+constexpr double kStream16Mean = 4.0;
+constexpr double kStream32Mean = 24.0;
+constexpr double kSmallMin = 8.0;
+constexpr double kSmallMax = 48.0;
+constexpr double kTallMean = 192.0;
 
 // The tiled GEMM's 32-bit offsets cover every operand of the expert FFNs.
 bool tiled_fits(const moe_problem_t* p) {
@@ -170,44 +150,41 @@ bool tiled_fits(const moe_problem_t* p) {
 Plan make_plan(const moe_problem_t* p, double mean_rows) {
   if (quantised(p)) {
     // fp8 x fp8, MXFP8 x MXFP4: the tiled kernel's quantised shapes
-    const int shape = (MOE_TILED_SMALL && mean_rows <= MOE_SMALL_MAX) ? TILED_SMALLQ
-                      : mean_rows <= MOE_TALL_MEAN ? TILED_TALL : TILED_WIDE;
+    const int shape = mean_rows <= kSmallMax ? TILED_SMALLQ
+                      : mean_rows <= kTallMean ? TILED_TALL : TILED_WIDE;
     return Plan{true, 0, tiled_bm(shape), shape};
   }
   const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16 && tiled_fits(p);
   int policy = p->tile_policy;
   const int ks = tiled_k_multiple_small();
-  const bool small_bf16 = MOE_SMALL_BF16 && p->w_dtype == MOE_BF16 &&
-                          (!p->I_shared || p->shared_w_dtype == MOE_BF16) && mean_rows <= MOE_SMALL_MAX;
+  const bool small_bf16 = p->w_dtype == MOE_BF16 && (!p->I_shared || p->shared_w_dtype == MOE_BF16) &&
+                          mean_rows <= kSmallMax;
   const bool small_fp8 = p->w_dtype == MOE_FP8_E4M3FN &&
                          (!p->I_shared || p->shared_w_dtype == MOE_FP8_E4M3FN) &&
-                         mean_rows > MOE_SMALL_MIN && mean_rows <= MOE_SMALL_MAX;
-  if (MOE_TILED_SMALL && policy == MOE_TILE_AUTO && tiled_ok && (small_fp8 || small_bf16) &&
+                         mean_rows > kSmallMin && mean_rows <= kSmallMax;
+  if (policy == MOE_TILE_AUTO && tiled_ok && (small_fp8 || small_bf16) &&
       p->D % ks == 0 && p->I % ks == 0 && p->I_shared % ks == 0)
     return Plan{true, 0, tiled_bm(TILED_SMALL), TILED_SMALL};
   if (policy == MOE_TILE_AUTO) policy = (tiled_ok && mean_rows > 48.0) ? MOE_TILE_LDS : MOE_TILE_STREAM;
   if (policy == MOE_TILE_LDS && tiled_ok) {
     // 256-row tiles read an expert's weights half as often; measured faster
     // while groups average a few hundred rows at most, 128-row tiles beyond
-    if (mean_rows <= MOE_TALL_MEAN) return Plan{true, 0, tiled_bm(TILED_TALL), TILED_TALL};
+    if (mean_rows <= kTallMean) return Plan{true, 0, tiled_bm(TILED_TALL), TILED_TALL};
     return Plan{true, 0, tiled_bm(TILED_WIDE), -1};
   }
-  int mt = mean_rows <= MOE_MT1_MEAN ? 1 : mean_rows <= MOE_MT2_MEAN ? 2 : 4;
+  int mt = mean_rows <= kStream16Mean ? 1 : mean_rows <= kStream32Mean ? 2 : 4;
   mt = std::min(mt, stream_max_mt(p->act_dtype));
   return Plan{false, mt, 16 * mt, -1};
 }
 
 // Down projection of the fused layer.  Where gate/up runs on 256-row tiles
-// (bf16, up to MOE_TALL_MEAN rows per expert) and D fills 512-wide blocks, the
-// down projection takes 128 x 512 tiles from a tile table of its own (build
-// knob MOE_DOWN_WIDE): its K is I rather than D, so a 256-row tile's blocks are
-// short, and 128-row blocks measured faster there (Qwen prefill down
-// projection 1.74 -> 1.64 ms) while gate/up keeps the 256-row tiles.
-#ifndef MOE_DOWN_WIDE
-#define MOE_DOWN_WIDE 1
-#endif
+// (bf16, up to kTallMean rows per expert) and D fills 512-wide blocks, the
+// down projection takes 128 x 512 tiles from a tile table of its own: its K is
+// I rather than D, so a 256-row tile's blocks are short, and 128-row blocks
+// measured faster there (Qwen prefill down projection 1.74 -> 1.64 ms) while
+// gate/up keeps the 256-row tiles.
 Plan down_plan(const moe_problem_t* p, const Plan& up) {
-  if (MOE_DOWN_WIDE && up.tiled && up.shape == TILED_TALL && !quantised(p) && p->D % 512 == 0)
+  if (up.tiled && up.shape == TILED_TALL && !quantised(p) && p->D % 512 == 0)
     return Plan{true, 0, tiled_bm(TILED_WIDE), -1};
   return up;
 }
@@ -238,7 +215,6 @@ void finish_grid(GArgs& g, const Plan& pl, bool gated) {
   g.shape = !pl.tiled ? -1 : pl.shape >= 0 ? pl.shape : pick_dense_shape(g, gated);
   for (int i = 0; i < g.nsets; ++i) {
     GSet& S = g.s[i];
-    S.nmajor = pl.tiled && MOE_TILED_NMAJOR;
     S.blocks_per_m = blocks_per_m(pl, g.shape, gated, S.n_out);
     S.block0 = b;
     S.bm = pl.bm;
@@ -247,16 +223,15 @@ void finish_grid(GArgs& g, const Plan& pl, bool gated) {
   g.total_blocks = b;
 }
 
-// The router is one dense group of T rows.  Large T: LDS-tiled GEMM.  Small T
-// (decode): streamed GEMM with the K dimension split into slices whose fp32
-// partial sums the top-k kernel adds in slice order, so enough wavefronts
-// stream the router weight.
-#ifndef MOE_ROUTER_TILED_T      // tokens from which the router runs on the LDS-tiled GEMM
-#define MOE_ROUTER_TILED_T 512
-#endif
+// The router is one dense group of T rows.  From kRouterTiledT tokens (and E
+// a multiple of 4: the tiled GEMM stores four output columns at a time) it
+// runs on the LDS-tiled GEMM; below (decode), on the streamed GEMM with the K
+// dimension split into slices whose fp32 partial sums the top-k kernel adds in
+// slice order, so enough wavefronts stream the router weight.
+constexpr int kRouterTiledT = 512;   // measured: Ling decode router 28 -> 20.5 us vs 1024
 Plan router_plan(const moe_problem_t* p) {
-  if (kTiledReady && p->act_dtype == MOE_BF16 && p->T >= MOE_ROUTER_TILED_T &&
-      p->tile_policy != MOE_TILE_STREAM &&
+  if (kTiledReady && p->act_dtype == MOE_BF16 && p->T >= kRouterTiledT &&
+      p->tile_policy != MOE_TILE_STREAM && p->E % 4 == 0 &&
       p->D % tiled_k_multiple() == 0 && tiled_offsets_fit(p->T, p->D, p->E, p->D, p->act_dtype))
     return Plan{true, 0, tiled_bm(TILED_WIDE), -1};
   int mt = p->T <= 16 ? 1 : p->T <= 32 ? 2 : 4;
@@ -264,25 +239,20 @@ Plan router_plan(const moe_problem_t* p) {
   return Plan{false, mt, 16 * mt, -1};
 }
 
-// K slices of the router: enough work items (tiled blocks or stream
-// wavefronts) to cover the GPU, each slice a multiple of 64 and at least
-// MOE_ROUTER_SLICE long (build-time knobs).
-#ifndef MOE_ROUTER_SLICE
-#define MOE_ROUTER_SLICE 256
-#endif
-#ifndef MOE_ROUTER_ITEMS
-#define MOE_ROUTER_ITEMS 512
-#endif
+// K slices of the router: the most slices (a divisor of D / 64) that keeps
+// each slice at least kRouterSlice long and the work items (tiled blocks or
+// stream wavefronts) at most kRouterItems.  Measured: finer splits make the
+// router faster and top-k slower by as much (more partial sums to add).
+constexpr int kRouterSlice = 256;
+constexpr int kRouterItems = 512;
 int router_splits(const moe_problem_t* p, const Plan& pl) {
   const int64_t m_tiles = (p->T + pl.bm - 1) / pl.bm;
   const int64_t items = pl.tiled ? m_tiles * tiled_blocks_n(TILED_NARROW, false, p->E)
                                  : m_tiles * stream_waves_n(false, p->E);
-  // the most slices (a divisor of K / 64) that keeps each slice at least
-  // MOE_ROUTER_SLICE long and the work items at most MOE_ROUTER_ITEMS
   const int K = p->D;
   int s = 1;
   for (int c = 2; c <= K / 64; ++c)
-    if ((K / 64) % c == 0 && K / c >= MOE_ROUTER_SLICE && items * c <= MOE_ROUTER_ITEMS) s = c;
+    if ((K / 64) % c == 0 && K / c >= kRouterSlice && items * c <= kRouterItems) s = c;
   return s;
 }
 
@@ -303,10 +273,12 @@ struct TimingRec {
   int stage;
   hipEvent_t a, b;
 };
-bool g_timing = false;
-uint32_t g_timing_mask = 0xffffffffu;   // stages timed while g_timing
-std::vector<TimingRec> g_recs;
-std::vector<hipEvent_t> g_pool;
+// The timing record belongs to the calling host thread (the library's only
+// state; see moe_timing_enable).
+thread_local bool g_timing = false;
+thread_local uint32_t g_timing_mask = 0xffffffffu;   // stages timed while g_timing
+thread_local std::vector<TimingRec> g_recs;
+thread_local std::vector<hipEvent_t> g_pool;
 
 hipEvent_t take_event() {
   if (!g_pool.empty()) {
@@ -519,11 +491,14 @@ moe_status_t moe_permute_workspace_size(const moe_problem_t* p, size_t* bytes) {
 }
 
 moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_t* counts,
-                         int32_t* offsets, int32_t* row_token, int32_t* row_of_slot, void* ws,
-                         size_t ws_bytes, void* stream) {
+                         int32_t* offsets, int32_t* row_token, int32_t* row_of_slot, const void* x,
+                         void* x_perm, void* ws, size_t ws_bytes, void* stream) {
   moe_status_t st = check_problem(p, false, true);
   if (st != MOE_OK) return st;
   if (!topk_idx || !counts || !offsets || !row_token || !row_of_slot) return MOE_ERR_NULL;
+  if ((x == nullptr) != (x_perm == nullptr)) return MOE_ERR_NULL;
+  if (x && (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(x_perm) % 16))
+    return MOE_ERR_SHAPE;
   const PermLayout L = perm_layout(p);
   if (L.total && !ws) return MOE_ERR_NULL;
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -539,6 +514,9 @@ moe_status_t moe_permute(const moe_problem_t* p, const int32_t* topk_idx, int32_
                               reinterpret_cast<int32_t*>(w + L.rank), counts, offsets, row_token,
                               row_of_slot, s));
   }
+  if (x)
+    MOE_LAUNCH(launch_gather_rows(x, row_token, offsets + p->E, p->T, p->T * p->k,
+                                  static_cast<int64_t>(p->D) * dt_bytes(p->act_dtype), x_perm, s));
   return MOE_OK;
 }
 
@@ -937,6 +915,25 @@ int32_t moe_stage_count(void) { return ST_COUNT; }
 
 const char* moe_stage_name(int32_t stage) {
   return (stage >= 0 && stage < ST_COUNT) ? kStageNames[stage] : "unknown";
+}
+
+moe_status_t moe_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink) return MOE_ERR_NULL;
+  if (bytes <= 0 || bytes % 16 || reinterpret_cast<uintptr_t>(buf) % 16) return MOE_ERR_SHAPE;
+  MOE_LAUNCH(launch_probe_hbm_read(buf, bytes, sink, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+int32_t moe_probe_mfma_sink_floats(void) { return probe_mfma_threads(); }
+
+moe_status_t moe_probe_mfma(int32_t dtype, const void* operands, int32_t iters, float* sink,
+                            double* flop, void* stream) {
+  if (!operands || !sink || !flop) return MOE_ERR_NULL;
+  if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3FN) return MOE_ERR_DTYPE;
+  if (iters <= 0 || reinterpret_cast<uintptr_t>(operands) % 16) return MOE_ERR_SHAPE;
+  MOE_LAUNCH(launch_probe_mfma(dtype == MOE_FP8_E4M3FN, operands, iters, sink, flop,
+                               static_cast<hipStream_t>(stream)));
+  return MOE_OK;
 }
 
 moe_status_t moe_debug_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int32_t n, void* stream) {

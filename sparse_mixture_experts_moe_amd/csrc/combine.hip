@@ -5,7 +5,8 @@
 // expert output row once and writes each token row once).  One block per (token
 // row, 1024-column chunk), so a small batch still spreads over the whole GPU;
 // every thread owns 8 consecutive hidden elements (16-byte accesses in bf16),
-// accumulates in fp32 in slot order and rounds once.
+// accumulates in fp32 in slot order and rounds once.  A token's column chunks
+// are consecutive blocks, so the blocks in flight read whole expert rows.
 #include "moe_kernels.h"
 
 namespace moe {
@@ -14,11 +15,6 @@ namespace {
 constexpr int THREADS = 128;
 constexpr int CHUNK = THREADS * 8;   // hidden elements per block
 constexpr int MAXK = 32;
-// Block order: 1 = a token's column chunks in consecutive blocks (the blocks
-// in flight read whole expert rows), 0 = chunk-major (token index fastest).
-#ifndef MOE_COMBINE_ROWMAJOR
-#define MOE_COMBINE_ROWMAJOR 1
-#endif
 
 // 8 elements as stored (bf16: 16 bytes; fp32: 32 bytes), loaded without use
 // so that several rows' loads can be in flight together
@@ -78,14 +74,9 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const void* __restrict
                                                           int D, int k, void* __restrict__ y) {
   __shared__ int32_t rows[MAXK];
   __shared__ float ws[MAXK];
-#if MOE_COMBINE_ROWMAJOR
   const int nch = (D + CHUNK - 1) / CHUNK;
   const int t = static_cast<int>(blockIdx.x / nch);
   const int chunk = static_cast<int>(blockIdx.x - static_cast<unsigned>(t) * nch);
-#else
-  const int t = blockIdx.x;
-  const int chunk = blockIdx.y;
-#endif
   if (threadIdx.x < k) {
     // rows outside [0, T*k) are dropped assignments
     const int32_t r = row_of_slot[static_cast<int64_t>(t) * k + threadIdx.x];
@@ -139,11 +130,7 @@ hipError_t launch_combine(const void* o_perm, const int32_t* row_of_slot, const 
                           hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int nch = (D + CHUNK - 1) / CHUNK;
-#if MOE_COMBINE_ROWMAJOR
   const dim3 grid(static_cast<unsigned>(static_cast<int64_t>(T) * nch));   // T * D < 2^31
-#else
-  const dim3 grid(T, nch);
-#endif
   if (dtype == DT_BF16)
     combine_kernel<DT_BF16><<<grid, THREADS, 0, s>>>(o_perm, row_of_slot, w, shared, T, D, k, y);
   else

@@ -36,43 +36,13 @@
 namespace moe {
 namespace {
 
-// 16-row weight fragments per wavefront (build-time tuning knob MOE_STREAM_NF:
-// 2, 4 or 8); a gated wavefront holds NF/2 gate and NF/2 up fragments
-#ifndef MOE_STREAM_NF
-#define MOE_STREAM_NF 4
-#endif
-constexpr int NF = MOE_STREAM_NF;
+// 16-row weight fragments per wavefront; a gated wavefront holds NF/2 gate
+// and NF/2 up fragments
+constexpr int NF = 4;
 constexpr int WROWS = 16 * NF;   // weight rows per wavefront
-static_assert(NF == 2 || NF == 4 || NF == 8, "fragments per wavefront");
 constexpr int WAVES = 4;         // wavefronts per block (consecutive N tiles)
 
-// Build-time tuning knobs (defaults are the measured choice):
-//   MOE_STREAM_NT  1: weight loads carry the non-temporal hint (read once)
-//   MOE_STREAM_U1  K-steps per register stage when tiles are one 16-row chunk
-#ifndef MOE_STREAM_NT
-#define MOE_STREAM_NT 0
-#endif
-#ifndef MOE_STREAM_U1
-#define MOE_STREAM_U1 2
-#endif
-//   MOE_STREAM_U2  K-steps per register stage when tiles are two 16-row chunks
-#ifndef MOE_STREAM_U2
-#define MOE_STREAM_U2 4
-#endif
-//   MOE_STREAM_AGPR  1: accumulators in AGPRs
-#ifndef MOE_STREAM_AGPR
-#define MOE_STREAM_AGPR 0
-#endif
-
-__device__ __forceinline__ uint4 load_w(const uint4* p) {
-#if MOE_STREAM_NT
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return uint4{v[0], v[1], v[2], v[3]};
-#else
-  return *p;
-#endif
-}
+__device__ __forceinline__ uint4 load_w(const uint4* p) { return *p; }
 
 template <int DT> struct Elt;
 template <> struct Elt<DT_F32> { static constexpr int bytes = 4; };
@@ -89,11 +59,6 @@ __global__ __launch_bounds__(64 * WAVES, 2) void stream_gemm_kernel(const GArgs 
   constexpr int AV = VecCount<ADT, U>::n;   // uint4 per lane per stage, A
   constexpr int BV = VecCount<WDT, U>::n;   // uint4 per lane per stage, B (per fragment)
   constexpr int KS = 32 * U;                // K elements per stage
-#if MOE_STREAM_AGPR
-  // an (empty) statement naming an accumulation register: the MFMAs then use
-  // the AGPR form and the accumulators leave the VGPRs to the register stages
-  asm volatile("" ::: "a0");
-#endif
   int si, group, row0, row1, nblk;
   if (!resolve_block(g, blockIdx.x, si, group, row0, row1, nblk)) return;
   const GSet& S = g.s[si];
@@ -276,10 +241,10 @@ hipError_t launch_one(const GArgs& g, hipStream_t s) {
 
 template <int MT, bool GATED, int ADT, int WDT, int ODT>
 hipError_t pick_u(const GArgs& g, hipStream_t s) {
-  // four-step stages when every K allows and registers do (bf16/fp8 operands,
-  // at most two 16-row chunks); fp32 operands always use two-step stages
-  if constexpr (MT <= 2 && ADT != DT_F32 && !(MT == 1 && MOE_STREAM_U1 == 2) &&
-                !(MT == 2 && MOE_STREAM_U2 == 2)) {
+  // K-steps per register stage (measured): four for two-chunk tiles of
+  // bf16/fp8 operands when every K allows, two otherwise (one- and four-chunk
+  // tiles, fp32 operands)
+  if constexpr (MT == 2 && ADT != DT_F32) {
     bool k128 = true;
     for (int i = 0; i < g.nsets; ++i)
       k128 = k128 && (g.s[i].K / (g.s[i].ksplit > 1 ? g.s[i].ksplit : 1)) % 128 == 0;

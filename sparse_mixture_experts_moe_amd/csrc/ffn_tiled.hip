@@ -79,9 +79,7 @@ namespace moe {
 namespace {
 
 constexpr int KS = 32;                    // K elements per MFMA sub-step
-#ifndef MOE_TILED_BK8A
-#define MOE_TILED_BK8A 128                // stage depth of fp8 x fp8 tiles (build-time knob)
-#endif
+constexpr int BK8A = 128;                 // stage depth of fp8 x fp8 tiles (64 measured 6 % slower)
 constexpr int LDS_CU = 160 * 1024;        // LDS per CU
 
 template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8, int BK_, int MF_, bool A8_ = false,
@@ -145,10 +143,8 @@ template <int RB> __device__ __forceinline__ int upos(int row, int c) {
 // sbase and lds are wave-uniform.  Issued through inline asm so the compiler
 // does not conservatively wait for every copy in flight before each LDS read;
 // completion is tracked explicitly with wait_vm below.
-// NT: the streaming (non-temporal) cache hint, for data read exactly once.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-template <bool NT = false>
 __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, const void* lds) {
   const uint32_t l = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds))));
@@ -156,12 +152,8 @@ __device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, const vo
   const uint32_t lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b)));
   const uint32_t hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32)));
   const uint64_t bs = static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32);
-  if constexpr (NT)
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(bs), "s"(l)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bs), "s"(l)
-                 : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(bs), "s"(l)
+               : "memory", "m0");
 }
 // Same with 4 bytes per lane (to lds + 4 * lane).
 __device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, const void* lds) {
@@ -199,44 +191,20 @@ template <int P, int M> __device__ __forceinline__ void wait_newer(int newer) {
   }
 }
 
-// Build-time tuning knob: MOE_TILED_REMAP 1 = XCD-aware block order (measured:
-// fewer bytes fetched by the gate/up launch but more by the down projection,
-// and slower overall on the fp8 prefill; off by default).
-#ifndef MOE_TILED_REMAP
-#define MOE_TILED_REMAP 0
-#endif
-// Same for the 32-row shape only.
-#ifndef MOE_SMALL_REMAP
-#define MOE_SMALL_REMAP 0
-#endif
-// 32-row shape: weight copies carry the streaming hint (each weight byte is
-// read once per launch; the activation rows are re-read by every N block)
-#ifndef MOE_SMALL_NT
-#define MOE_SMALL_NT 0
-#endif
 constexpr int NXCD = 8;   // XCDs; workgroup i is dispatched to XCD i % NXCD
-// Block order of the 256-row shape (MOE_TILED_XCDTILE 1): all N blocks of an
-// M-tile on one XCD (tile t on XCD t % NXCD), tiles interleaved across the
-// XCDs, so a tile's activation rows are fetched into one L2 instead of eight.
-// The default order puts N block n of every tile on XCD n, which instead
+// Block order of the 256-row shape: all N blocks of an M-tile on one XCD
+// (tile t on XCD t % NXCD), tiles interleaved across the XCDs, so a tile's
+// activation rows are fetched into one L2 instead of eight.  The other shapes
+// keep the launch order, which puts N block n of every tile on XCD n and so
 // shares an expert's weight slabs between its tiles: better where experts
 // have several tiles (the 128-row shapes, measured), worse where most have
 // one (the 256-row shape: Qwen prefill 4.73 -> 4.61 ms, Gemma level).
-#ifndef MOE_TILED_XCDTILE
-#define MOE_TILED_XCDTILE 1
-#endif
-#ifndef MOE_SMALL_XCDTILE       // the same order for the 32-row shape
-#define MOE_SMALL_XCDTILE 0
-#endif
-template <class C> constexpr bool xcdtile() {
-  return (MOE_TILED_XCDTILE && C::BM == 256) || (MOE_SMALL_XCDTILE && C::BM == 32);
-}
+template <class C> constexpr bool xcdtile() { return C::BM == 256; }
 
-#if MOE_TILED_XCDTILE || MOE_SMALL_XCDTILE
-// The XCD-tile order applies to grids without K slices or N-major sets.
+// The XCD-tile order applies to grids without K slices.
 __host__ __device__ inline bool xcdtile_ok(const GArgs& g) {
   for (int i = 0; i < g.nsets; ++i)
-    if (g.s[i].ksplit > 1 || g.s[i].nmajor) return false;
+    if (g.s[i].ksplit > 1) return false;
   return true;
 }
 // Physical grid of the XCD-tile order: each set's tiles padded to a multiple
@@ -265,52 +233,6 @@ __device__ __forceinline__ bool xcdtile_block(const GArgs& g, int b, int& logica
   }
   return false;
 }
-#endif
-template <class C> constexpr bool remapped() { return MOE_TILED_REMAP || (MOE_SMALL_REMAP && C::BM == 32); }
-
-#if MOE_TILED_REMAP || MOE_SMALL_REMAP
-// Logical block of a physical one.  Workgroups are dispatched round-robin over
-// the XCDs, so XCD x runs blocks x, x + 8, x + 16, ...; the remap gives each
-// XCD one contiguous, equal share of the blocks that exist (the M-tiles of a
-// few experts with all their N blocks), so an expert's weight slabs and an
-// M-tile's rows are fetched into one XCD's L2 instead of all eight.
-__device__ __forceinline__ bool remap_block(const GArgs& g, int& logical) {
-  int real = 0;
-  for (int i = 0; i < g.nsets; ++i) {
-    const GSet& S = g.s[i];
-    const int m = S.tiles ? min(S.n_tiles[0], S.m_slots) : S.m_slots;
-    real += m * S.blocks_per_m * (S.ksplit > 1 ? S.ksplit : 1);
-  }
-  const int per_xcd = (real + NXCD - 1) / NXCD;
-  const int b = blockIdx.x;
-  const int slot = b / NXCD;
-  if (slot >= per_xcd) return false;
-  int l = (b % NXCD) * per_xcd + slot;
-  if (l >= real) return false;
-  // back to the grid numbering resolve_block uses: the l-th valid (tile, N
-  // block, K slice) of a set, in the set's block order
-  for (int i = 0; i < g.nsets; ++i) {
-    const GSet& S = g.s[i];
-    const int m = S.tiles ? min(S.n_tiles[0], S.m_slots) : S.m_slots;
-    const int ks = S.ksplit > 1 ? S.ksplit : 1;
-    const int n = m * S.blocks_per_m * ks;
-    if (l < n) {
-      const int pair = l / ks, split = l - pair * ks;
-      int local;
-      if (S.nmajor) {          // N block by N block, the valid tiles of each
-        const int nb = pair / m;
-        local = nb * S.m_slots + (pair - nb * m);
-      } else {                 // tile by tile: the valid tiles come first
-        local = pair;
-      }
-      logical = S.block0 + local * ks + split;
-      return true;
-    }
-    l -= n;
-  }
-  return false;
-}
-#endif
 
 template <class C, bool GATED, int WDT, int ODT>
 __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GArgs g) {
@@ -325,14 +247,8 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   // the VGPRs stay free for fragments.
   asm volatile("" ::: "a0");
   int b = blockIdx.x;
-#if MOE_TILED_XCDTILE || MOE_SMALL_XCDTILE
   if constexpr (xcdtile<C>())
     if (xcdtile_ok(g) && !xcdtile_block(g, blockIdx.x, b)) return;
-#endif
-#if MOE_TILED_REMAP || MOE_SMALL_REMAP
-  if constexpr (remapped<C>())
-    if (!remap_block(g, b)) return;
-#endif
   int si, group, row0, row1, nblk;
   if (!resolve_block(g, b, si, group, row0, row1, nblk)) return;
   // the tile is the same for the whole block: keep it (and everything derived
@@ -421,8 +337,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
       dma16(a_off[k], a_base + st * ROWA, base + (wave * C::AL + k) * 1024);
     } else {
       const int i = k - C::AL;
-      dma16<C::BM == 32 && MOE_SMALL_NT>(b_off[i], b_base + st * C::ROWBW,
-                                         base + C::A_BYTES + (wave * C::BL + i) * 1024);
+      dma16(b_off[i], b_base + st * C::ROWBW, base + C::A_BYTES + (wave * C::BL + i) * 1024);
     }
   };
   // MX block scales: wavefront w < NSC copies one part of stage st's scales --
@@ -797,11 +712,9 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
 
 template <class C, bool GATED, int WDT, int ODT>
 hipError_t launch_one(const GArgs& g, hipStream_t s) {
-  int grid = remapped<C>() ? (g.total_blocks + NXCD - 1) / NXCD * NXCD : g.total_blocks;
-#if MOE_TILED_XCDTILE || MOE_SMALL_XCDTILE
+  int grid = g.total_blocks;
   if constexpr (xcdtile<C>())
     if (xcdtile_ok(g)) grid = xcdtile_grid(g);
-#endif
   tiled_gemm_kernel<C, GATED, WDT, ODT><<<grid, C::THREADS, 0, s>>>(g);
   return hipGetLastError();
 }
@@ -810,7 +723,8 @@ template <int BM, int BNW, int WM, int WN, int BPC, int MF>
 hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, int a_dtype, hipStream_t s) {
   using CB = Cfg<BM, BNW, WM, WN, BPC, false, 32, MF>;
   // fp8 weights 64 deep where three such stages fit in the block's LDS share
-  using C8 = Cfg<BM, BNW, WM, WN, BPC, true, (BPC == 1 ? 64 : 32), MF>;
+  constexpr bool W1 = BM == 128 && BNW == 512;
+  using C8 = Cfg<BM, BNW, (W1 ? 1 : WM), (W1 ? 8 : WN), BPC, true, (BPC == 1 ? 64 : 32), MF>;
   if (a_dtype == DT_MXFP8) {
     // MXFP8 x MXFP4: one block per CU, scaled 32x32x64 MFMAs, 128-deep stages
     if constexpr (BPC == 1) {
@@ -823,7 +737,7 @@ hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, int 
   if (a_dtype == DT_FP8) {
     // fp8 x fp8: one block per CU, 32x32x64 MFMAs
     if constexpr (BPC == 1) {
-      using CA = Cfg<BM, BNW, WM, WN, 1, true, MOE_TILED_BK8A, 32, true>;
+      using CA = Cfg<BM, BNW, WM, WN, 1, true, BK8A, 32, true>;
       if (w_dtype != DT_FP8 || out_dtype != DT_BF16) return hipErrorInvalidValue;
       return gated ? launch_one<CA, true, DT_FP8, DT_BF16>(g, s) : launch_one<CA, false, DT_FP8, DT_BF16>(g, s);
     }
@@ -844,35 +758,23 @@ hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, int 
 // x 32 weight rows, two blocks per CU, 128-deep stages (128-byte fp8 or
 // 256-byte bf16 weight-row requests, four MFMA sub-steps per stage) in a ring
 // of two or three.  The weights stream through the LDS ring, so a block keeps
-// its next stage in flight without holding it in registers.
-#ifndef MOE_SMALL_BNW
-#define MOE_SMALL_BNW 128     // build-time knobs: block width and blocks per CU
-#endif
-#ifndef MOE_SMALL_BPC
-#define MOE_SMALL_BPC (MOE_SMALL_BNW <= 256 ? 2 : 1)
-#endif
-#ifndef MOE_SMALL_BK
-#define MOE_SMALL_BK 128
-#endif
-// bf16 weights, K >= MOE_SMALL_DEEP_K: 256-deep stages instead (0 = never)
-#ifndef MOE_SMALL_DEEP
-#define MOE_SMALL_DEEP 1
-#endif
-#ifndef MOE_SMALL_DEEP_K
-#define MOE_SMALL_DEEP_K 2048
-#endif
+// its next stage in flight without holding it in registers.  bf16 weights
+// over a long K (at least kSmallDeepK) take 256-deep stages instead, one
+// block per CU (512-byte weight-row requests; measured on the Qwen decode
+// gate/up projection 1067 -> 1035 us; a short K keeps 128-deep stages).
+constexpr int kSmallBNW = 128;
+constexpr int kSmallBK = 128;
+constexpr int kSmallDeepK = 2048;
 hipError_t dispatch_small(const GArgs& g, bool gated, int w_dtype, int out_dtype, int a_dtype,
                           hipStream_t s) {
-  using C = Cfg<32, MOE_SMALL_BNW, 1, 4, MOE_SMALL_BPC, true, MOE_SMALL_BK, 16>;
-  using CB = Cfg<32, MOE_SMALL_BNW, 1, 4, MOE_SMALL_BPC, false, MOE_SMALL_BK, 16>;
-  // bf16 weights with a long K: 256-deep stages (512-byte weight-row
-  // requests), one block per CU
-  using CBD = Cfg<32, MOE_SMALL_BNW, 1, 4, 1, false, 256, 16>;
-  bool deep = MOE_SMALL_DEEP && w_dtype == DT_BF16;
+  using C = Cfg<32, kSmallBNW, 1, 4, 2, true, kSmallBK, 16>;
+  using CB = Cfg<32, kSmallBNW, 1, 4, 2, false, kSmallBK, 16>;
+  using CBD = Cfg<32, kSmallBNW, 1, 4, 1, false, 256, 16>;
+  bool deep = w_dtype == DT_BF16;
   for (int i = 0; i < g.nsets; ++i) {
     const int k = g.s[i].K / (g.s[i].ksplit > 1 ? g.s[i].ksplit : 1);
     if (k % C::BK) return hipErrorInvalidValue;
-    deep = deep && k % CBD::BK == 0 && k >= MOE_SMALL_DEEP_K;
+    deep = deep && k % CBD::BK == 0 && k >= kSmallDeepK;
   }
   if (a_dtype != DT_BF16 || out_dtype != DT_BF16) return hipErrorInvalidValue;
   if (w_dtype == DT_FP8)
@@ -902,7 +804,7 @@ hipError_t dispatch_smallq(const GArgs& g, bool gated, int w_dtype, int out_dtyp
 
 // weight rows per block of a shape
 int block_width(int shape) {
-  return shape == TILED_WIDE ? 512 : shape == TILED_SMALL ? MOE_SMALL_BNW : 256;
+  return shape == TILED_WIDE ? 512 : shape == TILED_SMALL ? kSmallBNW : 256;
 }
 
 }  // namespace
@@ -916,7 +818,7 @@ int tiled_k_multiple() { return 2 * KS; }
 // fp8 x fp8: K a multiple of the 128-deep stage (or of two 64-deep ones)
 int tiled_k_multiple_a8() { return 128; }
 
-int tiled_k_multiple_small() { return MOE_SMALL_BK; }
+int tiled_k_multiple_small() { return kSmallBK; }
 
 int tiled_blocks_n(int shape, bool gated, int n_out) {
   const int w = gated ? block_width(shape) / 2 : block_width(shape);

@@ -58,7 +58,6 @@ struct GSet {
   int32_t NB;               // weight rows: 2*I (gated) or N (plain)
   int32_t n_out;            // output columns: I (gated) or N (plain)
   int32_t act;              // gated activation
-  int32_t nmajor;           // 1: blocks ordered N block by N block (tiles fastest)
   void* out;                // output storage, row stride ldo elements
   int64_t ldo;
   const GTile* tiles;       // m-tile table, or null for dense tiles over [0, rows)
@@ -118,14 +117,9 @@ __device__ __forceinline__ bool resolve_block(const GArgs& g, int b, int& si, in
   const GSet& S = g.s[si];
   int local = b - S.block0;
   if (S.ksplit > 1) local /= S.ksplit;
-  int m;
-  if (S.nmajor) {            // consecutive blocks: same N block, consecutive tiles
-    nblk = local / S.m_slots;
-    m = local - nblk * S.m_slots;
-  } else {                   // consecutive blocks: same tile, consecutive N blocks
-    m = local / S.blocks_per_m;
-    nblk = local - m * S.blocks_per_m;
-  }
+  // consecutive blocks: same tile, consecutive N blocks
+  const int m = local / S.blocks_per_m;
+  nblk = local - m * S.blocks_per_m;
   if (S.tiles) {
     if (m >= S.n_tiles[0]) return false;
     const GTile t = S.tiles[m];
@@ -156,6 +150,12 @@ int perm_blocks(int T);
 hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* blk /*[nb*E]*/,
                           int32_t* local_rank /*[T*k]*/, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* row_of_slot, hipStream_t s);
+
+// x_perm[r] = x[row_token[r]] (row_bytes, a multiple of 16, per row) for the
+// rows r < min(rows, *n_rows) (n_rows: device pointer, offsets[E]); rows whose
+// token is outside [0, T) are left as they are.
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* n_rows, int T,
+                              int rows, int64_t row_bytes, void* x_perm, hipStream_t s);
 
 // Batches of at most perm_small_max_tokens() tokens: permutation and, when
 // tiles is not null, the M-tile table (group order or, spread, a fixed order
@@ -225,6 +225,16 @@ hipError_t launch_quant_rows_mx(const uint16_t* a, int rows, int cols, int64_t l
 
 // Decode n (multiple of 8) fp8 e4m3fn codes to bf16 with the GEMM's own decoder.
 hipError_t launch_fp8_decode(const uint8_t* codes, uint16_t* out, int n, hipStream_t s);
+
+// Measurement probes: a streaming read of `bytes` (a multiple of 16) with
+// eight 16-byte loads in flight per thread (sink: 1024 words, written only on
+// a magic XOR value); independent register-only MFMAs (bf16 16x16x32 or fp8
+// 32x32x64) on operands read from 64 KiB of random values, with the FLOP
+// count of the launch in *flop (sink: probe_mfma_threads() floats).
+int probe_mfma_threads();
+hipError_t launch_probe_hbm_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t s);
+hipError_t launch_probe_mfma(bool fp8, const void* operands, int iters, float* sink, double* flop,
+                             hipStream_t s);
 
 // Combine.
 hipError_t launch_combine(const void* o_perm, const int32_t* row_of_slot, const float* w,

@@ -119,16 +119,12 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
   row_of_slot[a] = r;
 }
 
-#ifndef MOE_PERM_STRIDE_NUM      // stride of the spread group order: about NUM / DEN of E
-#define MOE_PERM_STRIDE_NUM 1
-#define MOE_PERM_STRIDE_DEN 2
-#endif
 // Position of group g (< G) in a fixed stride permutation of the groups: a
 // stride of about G / 2, made coprime to G, so neighbouring groups land far
 // apart in the order.  (Odd start, steps of 2: the search reaches a unit mod
 // G, so it ends.)
 __device__ __forceinline__ int spread_rank(int g, int G) {
-  int a = (MOE_PERM_STRIDE_NUM * G / MOE_PERM_STRIDE_DEN + 1) | 1;
+  int a = (G / 2 + 1) | 1;
   for (;;) {
     int x = a, y = G;
     while (y) {
@@ -141,9 +137,6 @@ __device__ __forceinline__ int spread_rank(int g, int G) {
   }
   return static_cast<int>((static_cast<int64_t>(g) * a) % G);
 }
-#ifndef MOE_TILES_SPREAD         // 1: the multi-block path's tile table in the spread order too
-#define MOE_TILES_SPREAD 0
-#endif
 
 // Single block: each group's M-tiles.  With largest_first the groups are
 // ordered by descending row count (ties by group id) so the heaviest experts
@@ -175,15 +168,11 @@ __global__ __launch_bounds__(TILE_THREADS) void build_tiles_kernel(const int32_t
   __syncthreads();
   int rank = g;
   if (largest_first && g < G) {
-#if MOE_TILES_SPREAD
-    rank = spread_rank(g, G);
-#else
     rank = 0;
     for (int o = 0; o < G; ++o) {
       const int no = sz[o];
       rank += (no > n) || (no == n && o < g);
     }
-#endif
   }
   const bool two = tiles2 != nullptr;
   ntl[g] = 0;
@@ -247,12 +236,6 @@ __device__ __forceinline__ int block_inclusive_scan(int32_t* sc, int v) {
   return sc[i];
 }
 
-// Order of the groups' M-tiles when spread: 1 = a stride permutation of the
-// group ids (measured faster: concurrently running blocks then stream weights
-// from experts far apart), 0 = largest group first.
-#ifndef MOE_PERM_SCRAMBLE
-#define MOE_PERM_SCRAMBLE 1
-#endif
 // MW 64-bit mask words per expert: batches of at most 64 * MW tokens.
 template <int MW>
 __global__ __launch_bounds__(SCAN_THREADS) void perm_small_kernel(
@@ -303,24 +286,16 @@ __global__ __launch_bounds__(SCAN_THREADS) void perm_small_kernel(
     row_of_slot[a] = r;
   }
   if (!tiles) return;
-  // M-tiles of each group: groups in id order or, spread, in a fixed order
-  // that puts neighbouring groups far apart
+  // M-tiles of each group: groups in id order or, spread, in a fixed stride
+  // order that puts neighbouring groups far apart (measured faster than
+  // largest-first here: blocks that run together then stream weights from
+  // experts far apart)
   __shared__ int32_t sz[SCAN_THREADS];
   __shared__ int32_t grp[SCAN_THREADS];
   sz[tid] = tid < E ? c : 0;
   __syncthreads();
   int rank = tid;
-#if MOE_PERM_SCRAMBLE
   if (spread && tid < E) rank = spread_rank(tid, E);
-#else
-  if (spread && tid < E) {   // largest group first (ties by id)
-    rank = 0;
-    for (int o = 0; o < E; ++o) {
-      const int no = sz[o];
-      rank += (no > c) || (no == c && o < tid);
-    }
-  }
-#endif
   if (tid < E) grp[rank] = tid;
   __syncthreads();
   const int gg = tid < E ? grp[tid] : 0;           // group at rank position tid
@@ -338,6 +313,23 @@ __global__ __launch_bounds__(SCAN_THREADS) void perm_small_kernel(
     }
   }
   if (tid == SCAN_THREADS - 1) n_tiles[0] = min(tincl, max_tiles);
+}
+
+// The materialised permuted copy ("Qwen 3.5 MoE on Ironwood", MoE track: the
+// gather of the routed tokens into one contiguous buffer): row r of x_perm is
+// x[row_token[r]], for the rows the permutation filled (r < offsets[E]).  One
+// block per sorted row, 16-byte copies.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ x,
+                                                          const int32_t* __restrict__ row_token,
+                                                          const int32_t* __restrict__ n_rows, int T,
+                                                          int64_t row_bytes, char* __restrict__ x_perm) {
+  const int r = blockIdx.x;
+  if (r >= n_rows[0]) return;
+  const int t = row_token[r];
+  if (static_cast<unsigned>(t) >= static_cast<unsigned>(T)) return;   // not filled by the permutation
+  const uint4* src = reinterpret_cast<const uint4*>(x + static_cast<int64_t>(t) * row_bytes);
+  uint4* dst = reinterpret_cast<uint4*>(x_perm + static_cast<int64_t>(r) * row_bytes);
+  for (int64_t i = threadIdx.x; i < row_bytes / 16; i += blockDim.x) dst[i] = src[i];
 }
 
 }  // namespace
@@ -378,6 +370,15 @@ hipError_t launch_permute(const int32_t* idx, int T, int k, int E, int32_t* blk,
     perm_scatter_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
         idx, local_rank, blk, offsets, T, k, E, row_token, row_of_slot);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, const int32_t* row_token, const int32_t* n_rows, int T,
+                              int rows, int64_t row_bytes, void* x_perm, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  const int threads = row_bytes / 16 >= 256 ? 256 : 64;
+  gather_rows_kernel<<<rows, threads, 0, s>>>(static_cast<const char*>(x), row_token, n_rows, T, row_bytes,
+                                              static_cast<char*>(x_perm));
   return hipGetLastError();
 }
 

@@ -112,12 +112,10 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_softmax_kernel(
   select_topk<EPL>(v, lane, t, E, k, renorm, idx, wout);
 }
 
-// Few partial sums (at most MOE_TOPK_WAVE_SPLITS): one wavefront per token,
-// four tokens per block, each lane adding its experts' partial sums in slice
-// order (the same additions as above), so every wavefront selects at once.
-#ifndef MOE_TOPK_WAVE_SPLITS
-#define MOE_TOPK_WAVE_SPLITS 4
-#endif
+// Few partial sums (at most kWaveSplits): one wavefront per token, four tokens
+// per block, each lane adding its experts' partial sums in slice order (the
+// same additions as above), so every wavefront selects at once.
+constexpr int kWaveSplits = 4;
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_softmax_wave_kernel(
     const float* __restrict__ part, int splits, float* __restrict__ logits_out, int T, int E,
@@ -157,7 +155,7 @@ __global__ __launch_bounds__(256) void topk_softmax_wave_kernel(
 template <int EPL>
 void go(const float* part, int splits, float* logits_out, int T, int E, int k, int renorm,
         int32_t* idx, float* w, hipStream_t s) {
-  if (splits <= MOE_TOPK_WAVE_SPLITS)
+  if (splits <= kWaveSplits)
     topk_softmax_wave_kernel<EPL><<<(T + 3) / 4, 256, 0, s>>>(part, splits, logits_out, T, E, k,
                                                               renorm, idx, w);
   else

@@ -184,7 +184,23 @@ def test_null_and_workspace_errors(lib):
     assert lib.moe_layer(ctypes.byref(ps), ctypes.byref(args), fake, need, None) == B.MOE_ERR_NULL
     assert lib.moe_route(ctypes.byref(p), fake, fake, None, 0, fake, fake, None) == B.MOE_ERR_NULL
     assert lib.moe_combine(ctypes.byref(p), None, fake, fake, None, fake, None) == B.MOE_ERR_NULL
-    assert lib.moe_permute(ctypes.byref(p), fake, fake, fake, fake, fake, None, 0, None) == B.MOE_ERR_NULL
+    assert lib.moe_permute(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, None, 0,
+                           None) == B.MOE_ERR_NULL
+    nperm = B.moe_permute_workspace_size(p)
+    # x and x_perm go together, 16-byte aligned
+    assert lib.moe_permute(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, fake, nperm,
+                           None) == B.MOE_ERR_NULL
+    assert lib.moe_permute(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, fake, nperm,
+                           None) == B.MOE_ERR_NULL
+    assert lib.moe_permute(ctypes.byref(p), fake, fake, fake, fake, fake, fake + 8, fake, fake, nperm,
+                           None) == B.MOE_ERR_SHAPE
+    # measurement probes: sizes and dtypes are checked before any launch
+    flop = ctypes.c_double(0)
+    assert lib.moe_probe_hbm_read(fake, 100, fake, None) == B.MOE_ERR_SHAPE
+    assert lib.moe_probe_hbm_read(None, 1 << 20, fake, None) == B.MOE_ERR_NULL
+    assert lib.moe_probe_mfma(B.MOE_F32, fake, 10, fake, ctypes.byref(flop), None) == B.MOE_ERR_DTYPE
+    assert lib.moe_probe_mfma(B.MOE_BF16, fake, 0, fake, ctypes.byref(flop), None) == B.MOE_ERR_SHAPE
+    assert lib.moe_probe_mfma_sink_floats() > 0
     assert lib.moe_grouped_ffn(ctypes.byref(p), 0, 10, fake, None, fake, fake, None, fake, None,
                                fake, fake, fake, 1 << 20, None) == B.MOE_ERR_SHAPE
     assert lib.moe_debug_fp8_to_bf16(fake, fake, 7, None) == B.MOE_ERR_SHAPE

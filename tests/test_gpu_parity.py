@@ -3,10 +3,10 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import (f64, oracle_layer, oracle_routing_from_logits, oracle_rows, problem,
-                         rel_err, run_layer, to_device, tol_for)
+from gpu_helpers import (f64, oracle_inputs, oracle_layer, problem, rel_err, run_layer, to_device,
+                         tol_for)
 from oracle.formats import fp8_e4m3fn_table
-from oracle.moe import permute, router_logits, topk_softmax
+from oracle.moe import layer, permute, router_logits, topk_softmax
 from sparse_mixture_experts_moe_amd import binding as B
 from workloads import CONFIGS, generate, shrink
 
@@ -136,6 +136,29 @@ def test_layer_max_experts_and_k(T, policy):
     res = run_layer(wl, policy, logits_in=torch.from_numpy(ref["logits"]).cuda())
     _check_routing(res, ref)
     assert rel_err(f64(res["y"]), ref["y"]) <= tol_for(cfg)
+
+
+# A device router at T >= 512 with E not a multiple of 4: the LDS-tiled router
+# stores four columns at a time, so such problems take the streamed router
+@pytest.mark.parametrize("E", [10, 6])
+def test_device_router_expert_count_not_multiple_of_four(E):
+    cfg = shrink(CONFIGS["qwen_prefill"], T=512, D=256, E=E, k=2, I=64, I_shared=64, zipf=False)
+    wl = to_device(generate(cfg, seed=12))
+    ref = oracle_layer(wl)
+    p = problem(cfg)
+    logits = torch.empty((cfg.T, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    B.moe_route(p, wl.x, wl.wr, logits, False, idx, w)
+    torch.cuda.synchronize()
+    lr = ref["logits"].astype(np.float64)
+    assert np.max(np.abs(f64(logits) - lr)) <= 1e-5 * max(1.0, float(np.max(np.abs(lr))))
+    same = np.all(np.sort(idx.cpu().numpy(), 1) == np.sort(ref["idx"], 1), axis=1)
+    assert same.mean() >= 0.99
+    res = run_layer(wl)
+    same = np.all(np.sort(res["topk_idx"].cpu().numpy(), 1) == np.sort(ref["idx"], 1), axis=1)
+    assert same.mean() >= 0.99
+    assert rel_err(f64(res["y"])[same], ref["y"][same]) <= tol_for(cfg)
 
 
 # 256-row tiles with skewed loads: hot experts with two to four tiles next to
@@ -280,6 +303,84 @@ def test_moe_permute_entry(T, E, k):
         assert np.array_equal(d[name].cpu().numpy(), ref[name]), name
 
 
+@pytest.mark.parametrize("T,E,k,D,dt,bad", [(300, 64, 4, 256, "bf16", False), (1100, 16, 3, 192, "f32", False),
+                                             (4099, 256, 8, 512, "bf16", False), (700, 32, 2, 128, "bf16", True)])
+def test_moe_permute_materialised_gather(T, E, k, D, dt, bad):
+    """x_perm[r] = x[row_token[r]] bit for bit; with out-of-range ids the rows
+    past offsets[E] are left as they were."""
+    rng = np.random.default_rng(T + D)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    if bad:
+        idx[::5, 0] = E + 3
+    p = B.make_problem(T, D, E, k, 64, act_dtype=dt, w_dtype=dt)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    x = torch.randn(T, D, dtype=torch.float32).to(tdt).cuda()
+    xp = torch.full((T * k, D), 7.0, dtype=tdt, device="cuda")
+    d = {n: torch.empty(sz, dtype=torch.int32, device="cuda") for n, sz in
+         (("counts", E), ("offsets", E + 1), ("row_token", T * k), ("row_of_slot", T * k))}
+    n = B.moe_permute_workspace_size(p)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    B.moe_permute(p, torch.from_numpy(idx).cuda(), d["counts"], d["offsets"], d["row_token"],
+                  d["row_of_slot"], ws, n, x=x, x_perm=xp)
+    torch.cuda.synchronize()
+    valid = np.where(idx < E, idx, 0)
+    if bad:   # the oracle's permutation of the valid assignments only
+        flat = idx.reshape(-1)
+        keep = np.flatnonzero(flat < E)
+        order = keep[np.argsort(flat[keep], kind="stable")]
+        row_token = order // k
+    else:
+        row_token = permute(valid, E)[2]
+    filled = len(row_token)
+    xh, xph = x.cpu(), xp.cpu()
+    assert torch.equal(xph[:filled].view(torch.int16 if dt == "bf16" else torch.int32),
+                       xh[torch.from_numpy(row_token.astype(np.int64))].view(torch.int16 if dt == "bf16"
+                                                                              else torch.int32))
+    assert torch.all(xph[filled:] == 7.0)
+
+
+def test_grouped_ffn_on_materialised_rows_matches_gathered():
+    """The grouped FFN on x_perm (row_token = NULL) gives the gathered path's
+    output bit for bit, and both match the oracle."""
+    cfg = SMALL["qwen_ragged"]
+    wl = to_device(generate(cfg, seed=13))
+    ref = oracle_layer(wl, keep=True)
+    T, k, D, E = cfg.T, cfg.k, cfg.D, cfg.E
+    p = problem(cfg)
+    d = {n: torch.empty(sz, dtype=torch.int32, device="cuda") for n, sz in
+         (("counts", E), ("offsets", E + 1), ("row_token", T * k), ("row_of_slot", T * k))}
+    xp = torch.empty((T * k, D), dtype=torch.bfloat16, device="cuda")
+    n = B.moe_permute_workspace_size(p)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    B.moe_permute(p, torch.from_numpy(np.asarray(ref["idx"])).cuda(), d["counts"], d["offsets"],
+                  d["row_token"], d["row_of_slot"], ws, n, x=wl.x, x_perm=xp)
+    outs = []
+    for a, rt in ((wl.x, d["row_token"]), (xp, None)):
+        h = torch.empty((T * k, cfg.I), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((T * k, D), dtype=torch.bfloat16, device="cuda")
+        nf = B.moe_grouped_ffn_workspace_size(p, E, T * k)
+        wsf = torch.empty(max(nf, 1), dtype=torch.uint8, device="cuda")
+        B.moe_grouped_ffn(p, E, T * k, a, rt, d["offsets"], wl.w13, wl.s13, wl.w2, wl.s2, h, out, wsf, nf)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert rel_err(f64(outs[1]), ref["o_perm"]) <= tol_for(cfg)
+
+
+def test_measurement_probes_run():
+    """The HBM-read and MFMA probes the benchmark reports run and count FLOPs."""
+    buf = torch.randint(0, 255, (64 << 20,), dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    B.moe_probe_hbm_read(buf, buf.numel(), sink)
+    ops = torch.randn(65536, dtype=torch.float32)          # 64 KiB of operands for either type
+    nsink = B.moe_probe_mfma_sink_floats()
+    fs = torch.empty(nsink, dtype=torch.float32, device="cuda")
+    for dt, o in (("bf16", ops[:32768].to(torch.bfloat16)), ("fp8", ops.to(torch.float8_e4m3fn))):
+        flop = B.moe_probe_mfma(dt, o.view(torch.uint8).cuda(), 4, fs)
+        torch.cuda.synchronize()
+        assert flop > 0 and torch.isfinite(fs).all()
+
+
 def test_moe_combine_reproduces_gathered_rows():
     """o_perm := x gathered through the permutation gives y = x * sum(w) = x."""
     T, E, k, D = 200, 16, 4, 256
@@ -356,46 +457,41 @@ def test_moe_grouped_ffn_entry(name, policy):
 FULL = ["qwen_decode", "gemma", "ling_decode", "qwen_prefill", "ling_prefill"]
 
 
-def _sample_tokens(ref, T, n_rand=4, seed=0):
-    rng = np.random.default_rng(seed)
-    toks = {0, T - 1, *rng.integers(0, T, n_rand).tolist()}
-    # tokens in the first and last rows of the busiest expert (many tiles, ragged tail)
-    e = int(np.argmax(ref["counts"]))
-    r0, r1 = int(ref["offsets"][e]), int(ref["offsets"][e + 1])
-    toks.update({int(ref["row_token"][r0]), int(ref["row_token"][r1 - 1])})
-    return sorted(toks)
+def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """Largest over tokens of max|got - ref| / max|ref| within the token's row,
+    so an error confined to rows of small magnitude is not hidden by the
+    tensor-wide normalisation."""
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return float(np.max(np.abs(got - ref).max(axis=1) / den))
 
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_layer(name):
+    """Every element of y at the benchmark sizes, against the whole-layer oracle."""
     cfg = CONFIGS[name]
     print(f"[full-size] {name}: generating on GPU", flush=True)
     wl = generate(cfg, seed=0, weight_device="cuda")
     to_device(wl)
-    from gpu_helpers import oracle_inputs
-    x, wr, _, _ = oracle_inputs(wl)
+    x, wr, expert, shared = oracle_inputs(wl)
     logits_ref = router_logits(x, wr)
-    ref = oracle_routing_from_logits(logits_ref, cfg.k, cfg.E)
     print(f"[full-size] {name}: running moe_layer with oracle logits", flush=True)
     res = run_layer(wl, logits_in=torch.from_numpy(logits_ref).cuda())
+    y = f64(res["y"])
+    print(f"[full-size] {name}: oracle, whole layer", flush=True)
+    ref = layer(x, wr, cfg.k, expert, shared, cfg.act, cfg.act_shared, logits_in=logits_ref)
     _check_routing(res, ref)
-    toks = _sample_tokens(ref, cfg.T)
-    print(f"[full-size] {name}: oracle on tokens {toks}", flush=True)
-    yref = oracle_rows(wl, toks, ref["idx"], ref["w"])
-    err = rel_err(f64(res["y"][toks]), yref)
-    print(f"[full-size] {name}: rel err {err:.3e}", flush=True)
+    err, rerr = rel_err(y, ref["y"]), row_rel_err(y, ref["y"])
+    print(f"[full-size] {name}: rel err {err:.3e} (worst row {rerr:.3e})", flush=True)
     assert err <= tol_for(cfg)
-    # fully on device: logits within tolerance; top-k sets may flip only on near-ties
+    assert rerr <= 3 * tol_for(cfg)
+    # fully on device: logits within tolerance; top-k sets may flip only on
+    # near-ties; tokens whose set agrees match the oracle's y
     res2 = run_layer(wl)
     lg = f64(res2["logits"])
     assert np.max(np.abs(lg - logits_ref)) <= 1e-5 * max(1.0, float(np.max(np.abs(logits_ref))))
     same = np.all(np.sort(res2["topk_idx"].cpu().numpy(), 1) == np.sort(ref["idx"], 1), axis=1)
     print(f"[full-size] {name}: tokens whose top-k set differs: {int((~same).sum())}", flush=True)
     assert same.mean() >= 0.999
-    agree = [t for t in toks if same[t]]
-    if agree:
-        yref2 = oracle_rows(wl, agree, res2["topk_idx"].cpu().numpy(),
-                            res2["topk_w"].cpu().numpy().astype(np.float64))
-        assert rel_err(f64(res2["y"][agree]), yref2) <= tol_for(cfg)
-    del wl, res, res2
+    assert rel_err(f64(res2["y"])[same], ref["y"][same]) <= tol_for(cfg)
+    del wl, res, res2, ref, y
     torch.cuda.empty_cache()
