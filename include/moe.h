@@ -267,6 +267,29 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* args, voi
                        size_t ws_bytes, void* stream);
 
 /*
+ * moe_layer_noalloc -- moe_layer for callers that cannot allocate device
+ * memory (work under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same launches, with the workspace in a device array
+ * owned by the library (moe_layer_noalloc_max_bytes() bytes, 128 MiB, held
+ * on every GPU the library runs on until the process ends) instead of a
+ * caller buffer.  The caller still passes the inputs and outputs (args).
+ * Nothing is allocated: no hipMalloc, hipFree or allocating library call, and
+ * no timing events (stage timing is not recorded for these calls).
+ *   Problems whose moe_layer_workspace_size exceeds the array return
+ *   MOE_ERR_WORKSPACE before anything is enqueued (the decode-sized layers
+ *   fit: 9 MiB for 64 tokens of the Qwen3.5 layer, 106 MiB for 512 tokens of
+ *   the Ling layer; prefill-sized ones do not).
+ *   The array belongs to the device of `stream`, and every call on that
+ *   device shares it: calls that overlap on one device (concurrent streams,
+ *   or host threads) race on it and must be serialised by the caller.  It
+ *   keeps the last call's contents; nothing in it needs to start at zero.
+ *   Other errors are those of moe_layer; MOE_ERR_LAUNCH also covers a failure
+ *   to look up the array's device address.
+ */
+size_t moe_layer_noalloc_max_bytes(void);
+moe_status_t moe_layer_noalloc(const moe_problem_t* p, const moe_layer_args_t* args, void* stream);
+
+/*
  * moe_quantize_rows -- dynamic per-row fp8 quantisation ("Ling-2.6-1T with
  * SGLang-JAX" page, section 5, activation quantisation): for each row r,
  *   scale[r] = max_c |a[r][c]| / 448 in fp32 (448 = largest finite e4m3fn

@@ -66,6 +66,8 @@ _SIG = {
     "moe_combine": [ctypes.POINTER(MoeProblem), _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_layer_workspace_size": [ctypes.POINTER(MoeProblem), ctypes.POINTER(ctypes.c_size_t)],
     "moe_layer": [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeLayerArgs), _vp, ctypes.c_size_t, _vp],
+    "moe_layer_noalloc_max_bytes": [],
+    "moe_layer_noalloc": [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeLayerArgs), _vp],
     "moe_status_string": [ctypes.c_int],
     "moe_timing_enable": [ctypes.c_int32],
     "moe_timing_read": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32],
@@ -93,6 +95,7 @@ def lib():
             f.argtypes = argt
             f.restype = ctypes.c_int
         L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_layer_noalloc_max_bytes.restype = ctypes.c_size_t
         L.moe_stage_name.restype = ctypes.c_char_p
         _LIB = L
     return _LIB
@@ -191,6 +194,14 @@ def layer_args(**kw) -> MoeLayerArgs:
 def moe_layer(p: MoeProblem, args: MoeLayerArgs, ws, ws_bytes: int, stream=None):
     _check(lib().moe_layer(ctypes.byref(p), ctypes.byref(args), _p(ws), ws_bytes, _stream(stream)),
            "moe_layer")
+
+
+def moe_layer_noalloc_max_bytes() -> int:
+    return lib().moe_layer_noalloc_max_bytes()
+
+
+def moe_layer_noalloc(p: MoeProblem, args: MoeLayerArgs, stream=None):
+    _check(lib().moe_layer_noalloc(ctypes.byref(p), ctypes.byref(args), _stream(stream)), "moe_layer_noalloc")
 
 
 def moe_timing_enable(on: bool, stages=None):

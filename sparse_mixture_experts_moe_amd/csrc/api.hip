@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/moe.h"
@@ -276,6 +277,7 @@ struct TimingRec {
 // The timing record belongs to the calling host thread (the library's only
 // state; see moe_timing_enable).
 thread_local bool g_timing = false;
+thread_local bool g_no_events = false;   // set while moe_layer_noalloc runs: no event creation
 thread_local uint32_t g_timing_mask = 0xffffffffu;   // stages timed while g_timing
 thread_local std::vector<TimingRec> g_recs;
 thread_local std::vector<hipEvent_t> g_pool;
@@ -296,7 +298,7 @@ struct StageScope {
   hipStream_t s;
   hipEvent_t a = nullptr;
   StageScope(int st, hipStream_t st_s) : stage(st), s(st_s) {
-    if (g_timing && ((g_timing_mask >> st) & 1u) && (a = take_event()) &&
+    if (g_timing && !g_no_events && ((g_timing_mask >> st) & 1u) && (a = take_event()) &&
         hipEventRecord(a, s) != hipSuccess) {
       g_pool.push_back(a);
       a = nullptr;
@@ -858,6 +860,67 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
                               p->act_dtype, A->y, s));
   }
   return MOE_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free layer
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): moe_layer_noalloc runs moe_layer with its workspace in a fixed
+// device array instead of a caller buffer.  The host side names the array
+// only in hipGetSymbolAddress: each device holds its own copy at its own
+// address, taken once per device with that device current, and that address
+// is what the kernels receive.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(128) << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The scratch array's address on device `dev` (nullptr on failure).
+void* scratch_on(int dev) {
+  std::call_once(g_scratch_once[dev], [dev] {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    void* ptr = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+    if (cur >= 0 && cur != dev) (void)hipSetDevice(cur);
+  });
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_layer_noalloc_max_bytes(void) { return kScratchBytes; }
+
+moe_status_t moe_layer_noalloc(const moe_problem_t* p, const moe_layer_args_t* A, void* stream) {
+  size_t need = 0;
+  moe_status_t st = moe_layer_workspace_size(p, &need);
+  if (st != MOE_OK) return st;
+  if (need > kScratchBytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = -1;
+  if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_LAUNCH;
+  void* ws = scratch_on(dev);
+  if (!ws) return MOE_ERR_LAUNCH;
+  g_no_events = true;
+  st = moe_layer(p, A, ws, kScratchBytes, stream);
+  g_no_events = false;
+  return st;
 }
 
 moe_status_t moe_quantize_rows(const void* a, int32_t rows, int32_t cols, int64_t lda, uint8_t* q,

@@ -24,7 +24,7 @@ def lib():
 
 def declared():
     txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:moe_status_t|const char\*|int32_t)\s+(moe_\w+)\s*\(", txt, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:moe_status_t|const char\*|int32_t|size_t)\s+(moe_\w+)\s*\(", txt, re.M)))
 
 
 def test_header_declares_the_entry_points():
