@@ -549,13 +549,8 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
     }
   };
   // MFMAs of one sub-step, row fragment by row fragment; fragments past the
-  // tile's last row (i >= na, a uniform branch) are skipped.  When dst >= 0,
-  // copies K0..K1-1 of stage dst are spread between the MFMA groups so their
-  // issue overlaps the MFMAs.
-  auto mma = [&](const Frag& F, int dst, auto k0, auto k1) __attribute__((always_inline)) {
-    constexpr int K0 = decltype(k0)::value, NK = decltype(k1)::value - K0;
-    constexpr int G = TF * NKS;
-    constexpr int PER = (NK + G - 1) / G;
+  // tile's last row (i >= na, a uniform branch) are skipped.
+  auto mma = [&](const Frag& F) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TF; ++i) {
 #pragma unroll
@@ -586,10 +581,6 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
             }
           }
         }
-        const int gi = i * NKS + ks;
-#pragma unroll
-        for (int u = 0; u < PER; ++u)
-          if (gi * PER + u < NK && dst >= 0) issue_one(dst, K0 + gi * PER + u);
       }
     }
   };
@@ -602,7 +593,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   // the barrier, which also frees the slot of the stage just finished for the
   // stage S further on).  That stage's copies go out in H chunks: the first
   // in this sub-step, the others in the next stage's first H - 1 sub-steps.
-  // Sub-step t + 1's fragments are read while t's MFMAs run.
+  // A sub-step issues its chunk of copies first, then reads sub-step t + 1's
+  // fragments, then runs t's MFMAs: copies issued ahead of the LDS reads and
+  // MFMAs measured about 5% faster than copies spread among the MFMAs.
+  auto issue_chunk = [&](int st, auto c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = decltype(chunk_lo(c))::value; k < decltype(chunk_hi(c))::value; ++k) issue_one(st, k);
+  };
   auto step = [&](Frag& cur, Frag& nxt, int t, auto ph) __attribute__((always_inline)) {
     constexpr int PH = decltype(ph)::value;
     if constexpr (PH == H - 1) {
@@ -611,16 +608,18 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
       settle(cur);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      if (x + S < nst) {
+        issue_scales(x + S);
+        issue_chunk(x + S, std::integral_constant<int, 0>());
+      }
       readf(nxt, t + 1);   // t + 1 == nst * H reads a stale slot that is never used
-      if (x + S < nst) issue_scales(x + S);
-      using c0 = std::integral_constant<int, 0>;
-      mma(cur, x + S < nst ? x + S : -1, chunk_lo(c0()), chunk_hi(c0()));
+      mma(cur);
     } else {
       const int x = t / H - 1;         // its slot was freed by the last barrier
       settle(cur);                     // (decodes fp8 weights)
+      if (x >= 0 && x + S < nst) issue_chunk(x + S, std::integral_constant<int, PH + 1>());
       readf(nxt, t + 1);
-      using cc = std::integral_constant<int, PH + 1>;
-      mma(cur, x >= 0 && x + S < nst ? x + S : -1, chunk_lo(cc()), chunk_hi(cc()));
+      mma(cur);
     }
   };
 
