@@ -50,6 +50,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--policy", default="auto", choices=["auto", "stream", "lds"])
+    ap.add_argument("--combine", default="auto", choices=["auto", "separate", "fused"],
+                    help="where the layer combines the expert rows (default: the library's choice)")
     ap.add_argument("--act-quant", action="store_true",
                     help="dynamic per-token fp8 activations in the expert GEMMs (fp8-weight workloads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -221,7 +223,8 @@ def main():
     aq = (B.MOE_ACT_QUANT_MXFP8 if cfg.w_dtype == "mxfp4"
           else B.MOE_ACT_QUANT_FP8_ROW if args.act_quant else B.MOE_ACT_QUANT_NONE)
     p = B.make_problem(cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.act, cfg.act_shared,
-                       cfg.act_dtype, cfg.w_dtype, cfg.shared_w_dtype, args.policy, act_quant=aq)
+                       cfg.act_dtype, cfg.w_dtype, cfg.shared_w_dtype, args.policy, act_quant=aq,
+                       combine=args.combine)
     ws_bytes = B.moe_layer_workspace_size(p)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     y = torch.empty((cfg.T, cfg.D), dtype=wl.x.dtype, device="cuda")

@@ -77,6 +77,13 @@ extern "C" {
 #define MOE_ACT_QUANT_FP8_ROW  1   /* dynamic per-token fp8 (see below)      */
 #define MOE_ACT_QUANT_MXFP8    2   /* dynamic MXFP8 blocks (see below)       */
 
+/* where moe_layer combines the expert rows (moe_problem_t.combine) */
+#define MOE_COMBINE_AUTO      0    /* the library's choice: separate (measured
+                                      faster on every layer, see moe_layer)   */
+#define MOE_COMBINE_SEPARATE  1    /* a combine launch after the down projection */
+#define MOE_COMBINE_FUSED     2    /* in the down projection where it allows it,
+                                      else separate (see moe_layer)           */
+
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_NULL = 1,          /* a required pointer is NULL               */
@@ -105,6 +112,7 @@ typedef struct moe_problem {
   int32_t shared_w_dtype; /* shared W13s / W2s                               */
   int32_t tile_policy;    /* MOE_TILE_*                                      */
   int32_t act_quant;      /* MOE_ACT_QUANT_*: activations of the expert GEMMs */
+  int32_t combine;        /* MOE_COMBINE_*: moe_layer only                   */
 } moe_problem_t;
 
 /*
@@ -258,9 +266,23 @@ typedef struct moe_layer_args {
  * moe_layer -- the whole layer, every step enqueued on one stream with no
  * host synchronisation: route -> permute -> grouped FFN (routed experts and the
  * shared branch in the same launches) -> combine.  The workspace holds every
- * intermediate (logits, routing metadata, h, o, and with act_quant the fp8
- * copies of x and h with their row scales); its size depends only on the
- * problem.
+ * intermediate (logits, routing metadata, h, o, the combine's arrival
+ * counters, and with act_quant the fp8 copies of x and h with their row
+ * scales); its size depends only on the problem.
+ *   Combine: with MOE_COMBINE_FUSED, and where the down projection runs on
+ *   the LDS-tiled kernel with bf16 rows in one launch (bf16 activations,
+ *   routed and shared weights of one dtype), the combine runs inside the
+ *   down projection: each token is combined by the block that stores its
+ *   last expert row of a column block (owner computes, as the single-point
+ *   accumulation per token of the "Gemma-4 model optimisation report",
+ *   section 5.3), with the arithmetic of moe_combine (fp32 in slot order,
+ *   the shared row last, one rounding), so y is bit-identical to the
+ *   separate combine's.  Elsewhere, and with MOE_COMBINE_SEPARATE or
+ *   _AUTO, a moe_combine launch follows the down projection: the expert
+ *   rows have to cross between the GPU's XCDs (each with its own L2) either
+ *   way, and the fused form's device-scope stores and end-of-block counting
+ *   cost more than the separate launch (Ling decode layer 2.53 vs 2.41 ms,
+ *   Ling prefill 16.8 vs 14.4 ms, measured).
  */
 moe_status_t moe_layer_workspace_size(const moe_problem_t* p, size_t* bytes);
 moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* args, void* ws,

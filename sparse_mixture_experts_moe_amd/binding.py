@@ -19,12 +19,14 @@ MOE_F32, MOE_BF16, MOE_FP8_E4M3FN, MOE_MXFP4_E2M1 = 0, 1, 2, 3
 MOE_ACT_SILU, MOE_ACT_GELU_TANH = 0, 1
 MOE_TILE_AUTO, MOE_TILE_STREAM, MOE_TILE_LDS = 0, 1, 2
 MOE_ACT_QUANT_NONE, MOE_ACT_QUANT_FP8_ROW, MOE_ACT_QUANT_MXFP8 = 0, 1, 2
+MOE_COMBINE_AUTO, MOE_COMBINE_SEPARATE, MOE_COMBINE_FUSED = 0, 1, 2
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3FN, "mxfp4": MOE_MXFP4_E2M1}
 ACTS = {"silu": MOE_ACT_SILU, "gelu_tanh": MOE_ACT_GELU_TANH}
 POLICIES = {"auto": MOE_TILE_AUTO, "stream": MOE_TILE_STREAM, "lds": MOE_TILE_LDS}
+COMBINES = {"auto": MOE_COMBINE_AUTO, "separate": MOE_COMBINE_SEPARATE, "fused": MOE_COMBINE_FUSED}
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -40,7 +42,7 @@ class MoeError(RuntimeError):
 class MoeProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "D", "E", "k", "I", "I_shared", "act", "act_shared", "renormalize",
-        "act_dtype", "w_dtype", "shared_w_dtype", "tile_policy", "act_quant")]
+        "act_dtype", "w_dtype", "shared_w_dtype", "tile_policy", "act_quant", "combine")]
 
 
 _vp = ctypes.c_void_p
@@ -131,10 +133,11 @@ def status_string(status: int) -> str:
 
 def make_problem(T, D, E, k, I, I_shared=0, act="silu", act_shared="silu", act_dtype="bf16",
                  w_dtype="bf16", shared_w_dtype=None, tile_policy="auto",
-                 renormalize=True, act_quant=MOE_ACT_QUANT_NONE) -> MoeProblem:
+                 renormalize=True, act_quant=MOE_ACT_QUANT_NONE, combine="auto") -> MoeProblem:
     return MoeProblem(T, D, E, k, I, I_shared, ACTS[act], ACTS[act_shared], int(bool(renormalize)),
                       DTYPES[act_dtype], DTYPES[w_dtype],
-                      DTYPES[shared_w_dtype or w_dtype], POLICIES[tile_policy], int(act_quant))
+                      DTYPES[shared_w_dtype or w_dtype], POLICIES[tile_policy], int(act_quant),
+                      COMBINES[combine])
 
 
 def moe_route(p: MoeProblem, x, w_router, logits, logits_given: bool, topk_idx, topk_w,

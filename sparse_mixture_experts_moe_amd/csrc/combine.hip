@@ -5,8 +5,11 @@
 // expert output row once and writes each token row once).  One block per (token
 // row, 1024-column chunk), so a small batch still spreads over the whole GPU;
 // every thread owns 8 consecutive hidden elements (16-byte accesses in bf16),
-// accumulates in fp32 in slot order and rounds once.  A token's column chunks
+// accumulates in fp32 in slot order (a fused multiply-add per slot, the
+// shared row added last) and rounds once.  A token's column chunks
 // are consecutive blocks, so the blocks in flight read whole expert rows.
+#include <algorithm>
+
 #include "moe_kernels.h"
 
 namespace moe {
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const void* __restrict
           widen<DT>(raw[u], v);
           const float wj = ws[j];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] += wj * v[i];
+          for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
         }
       }
     }
@@ -123,7 +126,19 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const void* __restrict
   }
 }
 
+__global__ __launch_bounds__(256) void fill_i32_kernel(int32_t* __restrict__ p, int64_t n, int32_t v) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
 }  // namespace
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
+  fill_i32_kernel<<<static_cast<unsigned>(blocks), 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const void* o_perm, const int32_t* row_of_slot, const float* w,
                           const void* shared, int T, int D, int k, int dtype, void* y,

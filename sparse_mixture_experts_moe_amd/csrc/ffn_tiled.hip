@@ -43,10 +43,11 @@
 // eight MFMA sub-steps, its copies spread over them.
 //
 // Workgroup b runs on XCD b % 8, and each XCD has its own L2: the 256-row
-// shape maps all N blocks of an M-tile to one XCD (tiles interleaved across
-// XCDs) so the tile's activation rows are fetched once; the other shapes keep
-// N block n of every tile on XCD n, which shares an expert's weight slab
-// between its tiles.
+// shape and the bf16-weight 128 x 512 shape map all N blocks of a group of
+// consecutive M-tiles to one XCD (groups interleaved across XCDs), so the
+// tiles' activation rows are fetched into one L2 and an expert's weight slab
+// is shared by its tiles in the group; the other shapes keep N block n of
+// every tile on XCD n.
 //
 // With fp8 activations as well (dynamic per-token quantisation, "Ling-2.6-1T
 // with SGLang-JAX" page, section 5: fp8 tokens and fp8 weights straight into
@@ -87,6 +88,7 @@ template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8, int BK_, int 
 struct Cfg {
   static constexpr bool A8 = A8_;                     // fp8 activations (with fp8 weights)
   static constexpr bool W4 = W4_;                     // MXFP4 weights, MXFP8 activations (with A8)
+  static constexpr bool W8 = FP8;                     // one-byte weights (fp8, or e2m1 pairs with W4)
   static constexpr int MF = MF_;                      // MFMA tile: 16 (16x16x32) or 32 (32x32x16 / x64 fp8)
   static constexpr int BK = BK_;                      // K elements per stage
   static constexpr int KSUB = A8 ? 64 : KS;           // K elements per MFMA sub-step
@@ -191,40 +193,55 @@ template <int P, int M> __device__ __forceinline__ void wait_newer(int newer) {
   }
 }
 
-constexpr int NXCD = 8;   // XCDs; workgroup i is dispatched to XCD i % NXCD
-// Block order of the 256-row shape: all N blocks of an M-tile on one XCD
-// (tile t on XCD t % NXCD), tiles interleaved across the XCDs, so a tile's
-// activation rows are fetched into one L2 instead of eight.  The other shapes
-// keep the launch order, which puts N block n of every tile on XCD n and so
-// shares an expert's weight slabs between its tiles: better where experts
-// have several tiles (the 128-row shapes, measured), worse where most have
-// one (the 256-row shape: Qwen prefill 4.73 -> 4.61 ms, Gemma level).
-template <class C> constexpr bool xcdtile() { return C::BM == 256; }
+constexpr int NXCD = 8;       // XCDs; workgroup i is dispatched to XCD i % NXCD
+constexpr int XCD_CUS = 32;   // compute units per XCD
+// XCD-grouped block order: consecutive M-tiles are taken G at a time, and
+// all N blocks of such a group run on one XCD (group j on XCD j % NXCD,
+// groups interleaved across the XCDs).  A group's tiles' activation rows are
+// then fetched into one L2 instead of eight, and the weight slab of an N
+// block is shared by the group's tiles of one expert, which run side by side.
+// The 256-row shape takes one tile per group (its experts mostly have one
+// tile); the 128 x 512 shape with bf16 weights takes as many tiles as make
+// one block per CU of the XCD (Qwen-sized prefill 4.58 -> 4.39 ms).  The
+// other shapes keep the launch order (N block n of every tile on XCD n): with
+// fp8 weights the grouped order measured slower (Ling-sized prefill 14.40 ->
+// 15.04 ms) and fetched no fewer bytes, the blocks of a group drifting apart
+// within a few stages.
+template <class C> constexpr bool xcdtile() { return C::BM == 256 || (C::BM == 128 && C::BNW == 512 && !C::W8); }
+template <class C> __host__ __device__ inline int xcd_tiles(int bpm) {
+  return C::BM == 256 || bpm >= XCD_CUS ? 1 : XCD_CUS / bpm;
+}
 
-// The XCD-tile order applies to grids without K slices.
+// The XCD-grouped order applies to grids without K slices.
 __host__ __device__ inline bool xcdtile_ok(const GArgs& g) {
   for (int i = 0; i < g.nsets; ++i)
     if (g.s[i].ksplit > 1) return false;
   return true;
 }
-// Physical grid of the XCD-tile order: each set's tiles padded to a multiple
-// of NXCD, all of a tile's N blocks.
-__host__ __device__ inline int xcdtile_grid(const GArgs& g) {
+// Physical grid of the XCD-grouped order: each set's tiles padded to a
+// multiple of NXCD groups, all of a tile's N blocks.
+template <class C> __host__ __device__ inline int xcdtile_grid(const GArgs& g) {
   int n = 0;
-  for (int i = 0; i < g.nsets; ++i)
-    n += (g.s[i].m_slots + NXCD - 1) / NXCD * NXCD * g.s[i].blocks_per_m;
+  for (int i = 0; i < g.nsets; ++i) {
+    const int gt = NXCD * xcd_tiles<C>(g.s[i].blocks_per_m);
+    n += (g.s[i].m_slots + gt - 1) / gt * gt * g.s[i].blocks_per_m;
+  }
   return n;
 }
 // Logical block (resolve_block's numbering, tile-major) of physical block b
-// in the XCD-tile order; false if b has no tile.
-__device__ __forceinline__ bool xcdtile_block(const GArgs& g, int b, int& logical) {
+// in the XCD-grouped order; false if b has no tile.  Block b is the
+// (b / NXCD)-th of XCD x = b % NXCD: within a set, XCD x runs groups x,
+// x + NXCD, ... in turn, each group's tiles with all their N blocks.
+template <class C> __device__ __forceinline__ bool xcdtile_block(const GArgs& g, int b, int& logical) {
   for (int i = 0; i < g.nsets; ++i) {
     const GSet& S = g.s[i];
     const int bpm = S.blocks_per_m;
-    const int seg = (S.m_slots + NXCD - 1) / NXCD * NXCD * bpm;   // a multiple of NXCD
+    const int G = xcd_tiles<C>(bpm);
+    const int seg = (S.m_slots + NXCD * G - 1) / (NXCD * G) * (NXCD * G) * bpm;   // a multiple of NXCD
     if (b < seg) {
       const int x = b % NXCD, q = b / NXCD;
-      const int tile = x + NXCD * (q / bpm), n = q % bpm;
+      const int grp = x + NXCD * (q / (G * bpm)), e = q % (G * bpm);
+      const int tile = grp * G + e / bpm, n = e % bpm;
       if (tile >= S.m_slots) return false;
       logical = S.block0 + tile * bpm + n;
       return true;
@@ -232,6 +249,97 @@ __device__ __forceinline__ bool xcdtile_block(const GArgs& g, int b, int& logica
     b -= seg;
   }
   return false;
+}
+
+// 16 bytes read at device scope (four 4-byte loads that bypass this XCD's
+// non-coherent cache lines): rows another XCD's block wrote in this launch.
+__device__ __forceinline__ uint4 load16_device(const uint16_t* p) {
+  uint32_t* q = reinterpret_cast<uint32_t*>(const_cast<uint16_t*>(p));
+  return uint4{__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+               __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+               __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+               __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+}
+
+__device__ __forceinline__ void widen_bf16x8(const uint4& r, float (&v)[8]) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// The fused combine's part of a down-projection block (bf16 rows), after its
+// output stores: count the block's rows in, then combine the tokens whose
+// last rows these were.  list: LDS for 1 + (row1 - row0) ints.  Every
+// wavefront of the block calls it.
+template <int THREADS, int COLS>
+__device__ __forceinline__ void fused_combine_tail(const GFuse& F, const GSet& S, int row0, int row1,
+                                                   int nblk, int* list) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  // The block's rows were stored at device scope; once every wavefront's
+  // stores have completed they are visible to every XCD, before any counter
+  // the block bumps can be seen (so no cache write-back is needed here).
+  wait_vm<0>();
+  __syncthreads();
+  if (tid == 0) list[0] = 0;
+  __syncthreads();
+  if (tid < 64) {
+    for (int r = row0 + lane; r < row1; r += 64) {
+      const int t = S.out_token ? S.out_token[r] : r;
+      if (t < 0 || t >= F.T) continue;   // not a token row (rows come from the permutation)
+      const int old = __hip_atomic_fetch_add(F.cnt + static_cast<int64_t>(t) * F.nb + nblk, 1,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (old == F.expect - 1) list[1 + atomicAdd(&list[0], 1)] = t;
+    }
+  }
+  __syncthreads();
+  const int n = list[0];
+  constexpr int TPT = COLS / 8;          // threads per owned token, 8 columns each
+  constexpr int PASS = THREADS / TPT;    // tokens per pass of the block
+  static_assert(COLS % 8 == 0 && THREADS % TPT == 0, "combine split");
+  const int64_t Tk = static_cast<int64_t>(F.T) * F.k;
+  const uint16_t* o = static_cast<const uint16_t*>(F.o);
+  for (int u = tid / TPT; u < n; u += PASS) {
+    const int t = list[1 + u];
+    const int d = nblk * COLS + (tid % TPT) * 8;
+    if (d >= F.D) continue;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    // slots in groups of 8: the group's loads first, then the rows in slot order
+    for (int j0 = 0; j0 < F.k; j0 += 8) {
+      uint4 raw[8];
+      int rr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = j0 + e;
+        const int r = j < F.k ? F.row_of_slot[static_cast<int64_t>(t) * F.k + j] : -1;
+        rr[e] = (r >= 0 && r < Tk) ? r : -1;
+        raw[e] = load16_device(o + static_cast<int64_t>(rr[e] < 0 ? 0 : rr[e]) * F.D + d);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (rr[e] < 0) continue;
+        float v[8];
+        widen_bf16x8(raw[e], v);
+        const float wj = F.w[static_cast<int64_t>(t) * F.k + j0 + e];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, v[i], acc[i]);
+      }
+    }
+    if (F.o_sh) {
+      float v[8];
+      widen_bf16x8(load16_device(static_cast<const uint16_t*>(F.o_sh) + static_cast<int64_t>(t) * F.D + d), v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    uint32_t wv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wv[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i])) | (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(F.y) + static_cast<int64_t>(t) * F.D + d) =
+        uint4{wv[0], wv[1], wv[2], wv[3]};
+  }
 }
 
 template <class C, bool GATED, int WDT, int ODT>
@@ -248,7 +356,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   asm volatile("" ::: "a0");
   int b = blockIdx.x;
   if constexpr (xcdtile<C>())
-    if (xcdtile_ok(g) && !xcdtile_block(g, blockIdx.x, b)) return;
+    if (xcdtile_ok(g) && !xcdtile_block<C>(g, blockIdx.x, b)) return;
   int si, group, row0, row1, nblk;
   if (!resolve_block(g, b, si, group, row0, row1, nblk)) return;
   // the tile is the same for the whole block: keep it (and everything derived
@@ -671,6 +779,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   constexpr int NG = MF == 16 ? 1 : MF / 8;                      // column groups per fragment and lane
   const int col_w = n0 + wn * OCOLS;
   char* outb = static_cast<char*>(Sg.out) + split * Sg.split_stride * (ODT == DT_F32 ? 4 : 2);
+  const bool fuse = g.fc.cnt != nullptr;   // fused combine (ungated bf16 launches only)
 #pragma unroll
   for (int fg = 0; fg < (GATED ? WF / 2 : WF) * NG; ++fg) {
     const int f = fg / NG, g = fg % NG;
@@ -701,11 +810,23 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
       if constexpr (ODT == DT_BF16) {
         const uint32_t p0 = static_cast<uint32_t>(f32_to_bf16(v[0])) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
         const uint32_t p1 = static_cast<uint32_t>(f32_to_bf16(v[2])) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(outb) + o) = uint2{p0, p1};
+        if (!GATED && fuse) {
+          // rows the fused combine reads on other XCDs: device-scope stores,
+          // written through this XCD's cache
+          uint32_t* q = reinterpret_cast<uint32_t*>(reinterpret_cast<uint16_t*>(outb) + o);
+          __hip_atomic_store(q, p0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(q + 1, p1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(outb) + o) = uint2{p0, p1};
+        }
       } else {
         *reinterpret_cast<float4*>(reinterpret_cast<float*>(outb) + o) = float4{v[0], v[1], v[2], v[3]};
       }
     }
+  }
+  if constexpr (!GATED && ODT == DT_BF16) {
+    static_assert(C::LDS >= 4 * (C::BM + 1), "combine list");
+    if (g.fc.cnt) fused_combine_tail<C::THREADS, BNW>(g.fc, Sg, row0, row1, nblk, reinterpret_cast<int*>(smem));
   }
 }
 
@@ -713,7 +834,7 @@ template <class C, bool GATED, int WDT, int ODT>
 hipError_t launch_one(const GArgs& g, hipStream_t s) {
   int grid = g.total_blocks;
   if constexpr (xcdtile<C>())
-    if (xcdtile_ok(g)) grid = xcdtile_grid(g);
+    if (xcdtile_ok(g)) grid = xcdtile_grid<C>(g);
   tiled_gemm_kernel<C, GATED, WDT, ODT><<<grid, C::THREADS, 0, s>>>(g);
   return hipGetLastError();
 }

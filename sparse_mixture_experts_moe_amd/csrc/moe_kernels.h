@@ -69,6 +69,28 @@ struct GSet {
   int32_t bm;               // rows per m-tile
   int32_t ksplit;           // K slices (>1 only for plain fp32 outputs: partial sums)
   int64_t split_stride;     // output elements between the partial sums of two slices
+  const int32_t* out_token; // fused combine: token of output row r (null: r itself)
+};
+
+// Combine fused into the down projection (bf16 rows, tiled kernel, no K
+// slices): after a block has stored its output rows, each row adds one to
+// the arrival counter of (its token, the block's N block).  The block whose
+// addition completes a counter (expect arrivals: the token's k routed rows
+// and its shared row) owns that token's columns of the N block: it sums the
+// token's rows exactly as the separate combine does (fp32, slot order, the
+// shared row last, one rounding) and writes y.  The owner is whichever block
+// arrives last, but the sum does not depend on it, so y is bit-identical to
+// the separate combine's.
+struct GFuse {
+  int32_t* cnt;                // [T][nb] arrival counters, zero at launch; null: no fused combine
+  const int32_t* row_of_slot;  // [T*k] routed row of slot (t, j)
+  const float* w;              // [T*k] routing weight of slot (t, j)
+  const void* o;               // [T*k][D] routed rows
+  const void* o_sh;            // [T][D] shared rows, or null
+  void* y;                     // [T][D]
+  int32_t T, D, k;
+  int32_t nb;                  // N blocks of the launch (counters per token)
+  int32_t expect;              // arrivals per (token, N block)
 };
 
 struct GArgs {
@@ -76,6 +98,7 @@ struct GArgs {
   int32_t nsets;
   int32_t total_blocks;
   int32_t shape;            // tiled kernel: TILED_* block shape (host-side choice)
+  GFuse fc;
 };
 
 // ------------------------------------------------------------------ device helpers
@@ -237,6 +260,9 @@ hipError_t launch_probe_mfma(bool fp8, const void* operands, int iters, float* s
                              hipStream_t s);
 
 // Combine.
+// Sets n int32 values to v (a kernel, so it can be captured in a graph).
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
 hipError_t launch_combine(const void* o_perm, const int32_t* row_of_slot, const float* w,
                           const void* shared, int T, int D, int k, int dtype, void* y,
                           hipStream_t s);

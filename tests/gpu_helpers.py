@@ -79,10 +79,10 @@ class PrefetchExperts:
             f.cancel()
 
 
-def problem(cfg, policy="auto", renormalize=True, act_quant=0) -> B.MoeProblem:
+def problem(cfg, policy="auto", renormalize=True, act_quant=0, combine="auto") -> B.MoeProblem:
     return B.make_problem(cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.act, cfg.act_shared,
                           cfg.act_dtype, cfg.w_dtype, cfg.shared_w_dtype, policy, renormalize,
-                          act_quant)
+                          act_quant, combine)
 
 
 def to_device(wl, dev="cuda"):
@@ -103,8 +103,8 @@ def f64(t: torch.Tensor) -> np.ndarray:
 def run_layer(wl, policy="auto", logits_in=None, want=("logits_out", "topk_idx_out", "topk_w_out",
                                                        "counts_out", "offsets_out",
                                                        "row_token_out", "row_of_slot_out"),
-              renormalize=True, act_quant=0):
-    p = problem(wl.cfg, policy, renormalize, act_quant)
+              renormalize=True, act_quant=0, combine="auto"):
+    p = problem(wl.cfg, policy, renormalize, act_quant, combine)
     res = B.run_layer(p, wl.x, wl.w13, wl.w2, w_router=wl.wr, s13=wl.s13, s2=wl.s2,
                       w13_shared=wl.w13s, s13_shared=wl.s13s, w2_shared=wl.w2s, s2_shared=wl.s2s,
                       logits_in=logits_in, want=want)

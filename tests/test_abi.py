@@ -70,6 +70,8 @@ def _ok_problem(**over):
     (dict(act_dtype=B.MOE_MXFP4_E2M1), B.MOE_ERR_DTYPE),               # weights-only format
     (dict(act_quant=1), B.MOE_ERR_UNSUPPORTED),                       # fp32 layer: no fp8 path
     (dict(renormalize=0), B.MOE_OK),
+    (dict(combine=3), B.MOE_ERR_UNSUPPORTED), (dict(combine=-1), B.MOE_ERR_UNSUPPORTED),
+    (dict(combine=B.MOE_COMBINE_SEPARATE), B.MOE_OK), (dict(combine=B.MOE_COMBINE_FUSED), B.MOE_OK),
 ])
 def test_validation_codes(lib, over, status):
     p = _ok_problem(**over)

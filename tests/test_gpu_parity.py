@@ -27,8 +27,8 @@ SMALL = {
                               zipf=False),
     "big_groups_fp8": shrink(CONFIGS["ling_prefill"], T=1030, D=320, E=4, k=2, I=128, I_shared=192),
     # fp8 weights, about 550 rows per expert, D and I filling whole 512-wide
-    # blocks: the 128 x 512 kernel that keeps the weight tile in registers,
-    # with ragged last tiles, and K = D, I not a multiple of six stages
+    # blocks: the 128 x 512 fp8 shape over several tiles per expert with
+    # ragged last tiles, and K = D, I not a multiple of six stages
     "wide_fp8": shrink(CONFIGS["ling_prefill"], T=1100, D=1024, E=4, k=2, I=768, I_shared=256),
     # fp8 weights, about 12 rows per expert with Zipf-skewed loads (empty experts
     # and experts over 32 rows): the automatic policy's 32-row tiled shape
