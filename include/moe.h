@@ -41,7 +41,11 @@
  *    weights MXFP4_E2M1, act_quant MXFP8} (W4A8); anything else is
  *    MOE_ERR_UNSUPPORTED (no silent fallback).
  *  - Limits: 1 <= k <= min(E, 32); E <= 1024; D, I, I_shared multiples of 64;
- *    T*k and T*max(D, I) below 2^31.  T == 0 is valid and enqueues nothing.
+ *    T*k below 2^31.  Element offsets are 64-bit; the LDS-tiled GEMM
+ *    addresses each activation operand (x, h) and each expert's weights with
+ *    32-bit byte offsets, so where one of them reaches 4 GiB the layer runs
+ *    the register-streamed GEMM instead (with act_quant, which needs the
+ *    tiled GEMM: MOE_ERR_SHAPE).  T == 0 is valid and enqueues nothing.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

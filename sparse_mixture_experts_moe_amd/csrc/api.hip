@@ -75,15 +75,20 @@ void set_scales(const moe_problem_t* p, GSet& S, const void* a_scale, int32_t a_
 bool w_scaled(int w_dtype) { return w_dtype == MOE_FP8_E4M3FN || w_dtype == MOE_MXFP4_E2M1; }
 
 // Checks common to every entry point.
+bool tiled_fits(const moe_problem_t* p);
+
 moe_status_t check_problem(const moe_problem_t* p, bool need_ffn, bool need_router) {
   if (!p) return MOE_ERR_NULL;
   if (p->T < 0 || p->D <= 0 || p->D % 64 || p->E < 1 || p->E > 1024) return MOE_ERR_SHAPE;
   if (need_router && (p->k < 1 || p->k > 32 || p->k > p->E)) return MOE_ERR_SHAPE;
   if (need_ffn && (p->I <= 0 || p->I % 64 || p->I_shared < 0 || p->I_shared % 64))
     return MOE_ERR_SHAPE;
+  // Row indices are int32 (T*k rows); element offsets are 64-bit everywhere
+  // except the LDS-tiled GEMM's per-lane byte offsets, which the plan checks
+  // (tiled_fits: bf16 layers fall back to the register-streamed GEMM, the
+  // quantised modes, tiled only, are refused below).
   const int64_t Tk = static_cast<int64_t>(p->T) * std::max(p->k, 1);
-  const int64_t wide = std::max<int64_t>({p->D, p->I, p->I_shared, p->E});
-  if (Tk >= (int64_t(1) << 31) || (Tk + p->T) * wide >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  if (Tk >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
   if (!dt_ok(p->act_dtype) || !wdt_ok(p->w_dtype) || !wdt_ok(p->shared_w_dtype)) return MOE_ERR_DTYPE;
   if (!act_ok(p->act) || !act_ok(p->act_shared)) return MOE_ERR_DTYPE;
   if (p->tile_policy < MOE_TILE_AUTO || p->tile_policy > MOE_TILE_LDS) return MOE_ERR_DTYPE;
@@ -110,6 +115,7 @@ moe_status_t check_problem(const moe_problem_t* p, bool need_ffn, bool need_rout
     if (p->D % km || p->I % km || p->I_shared % km) return MOE_ERR_UNSUPPORTED;
     const int qm = quant_max_cols();
     if (p->D > qm || p->I > qm || p->I_shared > qm) return MOE_ERR_UNSUPPORTED;
+    if (!tiled_fits(p)) return MOE_ERR_SHAPE;
   }
   return MOE_OK;
 }

@@ -71,6 +71,7 @@ def _ok_problem(**over):
     (dict(act_quant=1), B.MOE_ERR_UNSUPPORTED),                       # fp32 layer: no fp8 path
     (dict(renormalize=0), B.MOE_OK),
     (dict(combine=3), B.MOE_ERR_UNSUPPORTED), (dict(combine=-1), B.MOE_ERR_UNSUPPORTED),
+    (dict(T=2 ** 22), B.MOE_OK),                                      # (T*k + T) * D past 2^31
     (dict(combine=B.MOE_COMBINE_SEPARATE), B.MOE_OK), (dict(combine=B.MOE_COMBINE_FUSED), B.MOE_OK),
 ])
 def test_validation_codes(lib, over, status):
@@ -94,6 +95,8 @@ def _fp8_problem(**over):
     (dict(tile_policy=B.MOE_TILE_STREAM), B.MOE_ERR_UNSUPPORTED),
     (dict(D=192), B.MOE_ERR_UNSUPPORTED), (dict(I=64), B.MOE_ERR_UNSUPPORTED),   # K multiple of 128
     (dict(I_shared=0), B.MOE_OK), (dict(D=32768), B.MOE_ERR_UNSUPPORTED),
+    (dict(T=200000, D=8192), B.MOE_OK),         # past 2^31 elements, x under 4 GiB
+    (dict(T=300000, D=8192), B.MOE_ERR_SHAPE),  # x past 4 GiB: the tiled GEMM (the only fp8 x fp8 one) cannot
 ])
 def test_act_quant_validation(lib, over, status):
     p = _fp8_problem(**over)

@@ -6,7 +6,7 @@ import torch
 from gpu_helpers import (f64, oracle_inputs, oracle_layer, problem, rel_err, run_layer, to_device,
                          tol_for)
 from oracle.formats import fp8_e4m3fn_table
-from oracle.moe import layer, permute, router_logits, topk_softmax
+from oracle.moe import layer, layer_tokens, permute, router_logits, topk_softmax
 from sparse_mixture_experts_moe_amd import binding as B
 from workloads import CONFIGS, generate, shrink
 
@@ -498,4 +498,35 @@ def test_full_size_layer(name):
     assert same.mean() >= 0.999
     assert rel_err(f64(res2["y"])[same], ref["y"][same]) <= tol_for(cfg)
     del wl, res, res2, ref, y
+    torch.cuda.empty_cache()
+
+
+def test_layer_past_2e31_elements():
+    """A layer whose permuted expert rows o [T*k, D] pass 2^31 elements (64-bit
+    offsets everywhere but the tiled GEMM's per-operand 32-bit byte offsets),
+    against the oracle on every token with a row past element 2^31 that a
+    sample draws, plus random tokens and the first and last."""
+    cfg = shrink(CONFIGS["ling_prefill"], T=36000, D=8192, E=16, k=8, I=256, I_shared=256)
+    assert cfg.T * cfg.k * cfg.D > 2 ** 31
+    print("[large-T] generating", flush=True)
+    wl = generate(cfg, seed=5, weight_device="cuda")
+    to_device(wl)
+    x, wr, expert, shared = oracle_inputs(wl)
+    logits = router_logits(x, wr)
+    idx, w = topk_softmax(logits, cfg.k)
+    _, _, row_token, _ = permute(idx, cfg.E)
+    print("[large-T] running moe_layer with oracle logits", flush=True)
+    res = run_layer(wl, logits_in=torch.from_numpy(logits).cuda(), want=("topk_idx_out", "row_token_out"))
+    assert np.array_equal(res["topk_idx"].cpu().numpy(), idx)
+    assert np.array_equal(res["row_token"].cpu().numpy(), row_token)
+    late = np.unique(row_token[2 ** 31 // cfg.D:])     # tokens with a row past element 2^31
+    rng = np.random.default_rng(0)
+    toks = sorted(set(rng.choice(late, 48, replace=False).tolist())
+                  | set(rng.choice(cfg.T, 16, replace=False).tolist()) | {0, cfg.T - 1})
+    print(f"[large-T] oracle on {len(toks)} tokens", flush=True)
+    ref = layer_tokens(toks, x, idx, w, expert, shared, cfg.act, cfg.act_shared)
+    err = rel_err(f64(res["y"])[toks], ref)
+    print(f"[large-T] rel err {err:.3e}", flush=True)
+    assert err <= tol_for(cfg)
+    del wl, res
     torch.cuda.empty_cache()
