@@ -41,7 +41,9 @@
  *    weights MXFP4_E2M1, act_quant MXFP8} (W4A8); anything else is
  *    MOE_ERR_UNSUPPORTED (no silent fallback).
  *  - Limits: 1 <= k <= min(E, 32); E <= 1024; D, I, I_shared multiples of 64;
- *    T*k below 2^31.  Element offsets are 64-bit; the LDS-tiled GEMM
+ *    T*k below 2^31 and the launch grids within int32 ((T*k/16 + T/16 + E + 2)
+ *    * (max(D, I, I_shared, E)/64 + 1) below 2^31).  Element offsets are
+ *    64-bit; the LDS-tiled GEMM
  *    addresses each activation operand (x, h) and each expert's weights with
  *    32-bit byte offsets, so where one of them reaches 4 GiB the layer runs
  *    the register-streamed GEMM instead (with act_quant, which needs the
@@ -350,7 +352,8 @@ moe_status_t moe_quantize_rows(const void* a, int32_t rows, int32_t cols, int64_
 moe_status_t moe_quantize_rows_mx(const void* a, int32_t rows, int32_t cols, int64_t lda, uint8_t* q,
                                   uint8_t* scale, void* stream);
 
-/* Human-readable name of a status code (static string). */
+/* Human-readable name of a status code (static string; "unknown status" for
+ * any other value). */
 const char* moe_status_string(moe_status_t status);
 
 /*

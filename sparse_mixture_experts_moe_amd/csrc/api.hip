@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstring>
 #include <mutex>
 #include <vector>
 
@@ -89,6 +90,10 @@ moe_status_t check_problem(const moe_problem_t* p, bool need_ffn, bool need_rout
   // quantised modes, tiled only, are refused below).
   const int64_t Tk = static_cast<int64_t>(p->T) * std::max(p->k, 1);
   if (Tk >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+  // launch grids are int32: row tiles (16 rows at the least, routed and
+  // shared) times column blocks (64 columns at the least) stay below 2^31
+  const int64_t wide = std::max<int64_t>({p->D, p->I, p->I_shared, p->E});
+  if ((Tk / 16 + p->T / 16 + p->E + 2) * (wide / 64 + 1) >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
   if (!dt_ok(p->act_dtype) || !wdt_ok(p->w_dtype) || !wdt_ok(p->shared_w_dtype)) return MOE_ERR_DTYPE;
   if (!act_ok(p->act) || !act_ok(p->act_shared)) return MOE_ERR_DTYPE;
   if (p->tile_policy < MOE_TILE_AUTO || p->tile_policy > MOE_TILE_LDS) return MOE_ERR_DTYPE;
@@ -254,7 +259,7 @@ Plan router_plan(const moe_problem_t* p) {
 constexpr int kRouterSlice = 256;
 constexpr int kRouterItems = 512;
 int router_splits(const moe_problem_t* p, const Plan& pl) {
-  const int64_t m_tiles = (p->T + pl.bm - 1) / pl.bm;
+  const int64_t m_tiles = (static_cast<int64_t>(p->T) + pl.bm - 1) / pl.bm;
   const int64_t items = pl.tiled ? m_tiles * tiled_blocks_n(TILED_NARROW, false, p->E)
                                  : m_tiles * stream_waves_n(false, p->E);
   const int K = p->D;
@@ -452,7 +457,7 @@ hipError_t launch_router(const moe_problem_t* p, const void* x, const void* wr, 
   S.out = part;
   S.ldo = p->E;
   S.rows = p->T;
-  S.m_slots = (p->T + pl.bm - 1) / pl.bm;
+  S.m_slots = static_cast<int32_t>((static_cast<int64_t>(p->T) + pl.bm - 1) / pl.bm);
   S.ksplit = splits;
   S.split_stride = static_cast<int64_t>(p->T) * p->E;
   finish_grid(g, pl, false);
@@ -465,7 +470,11 @@ hipError_t launch_router(const moe_problem_t* p, const void* x, const void* wr, 
 extern "C" {
 
 const char* moe_status_string(moe_status_t st) {
-  switch (st) {
+  // C callers may pass any int: read the bits rather than the enum value
+  // (a C++ enum holding a value outside its range is undefined)
+  int32_t v;
+  std::memcpy(&v, &st, sizeof v);
+  switch (v) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL: return "null pointer";
     case MOE_ERR_SHAPE: return "size out of the supported range";
@@ -654,6 +663,28 @@ moe_status_t moe_combine(const moe_problem_t* p, const void* o_perm, const int32
   return MOE_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// The layer's problem and the pointers it requires.
+moe_status_t check_layer_args(const moe_problem_t* p, const moe_layer_args_t* A) {
+  moe_status_t st = check_problem(p, true, true);
+  if (st != MOE_OK) return st;
+  if (!A || !A->x || !A->w13 || !A->w2 || !A->y) return MOE_ERR_NULL;
+  if (!A->logits_in && !A->w_router) return MOE_ERR_NULL;
+  if (w_scaled(p->w_dtype) && (!A->s13 || !A->s2)) return MOE_ERR_NULL;
+  if (p->I_shared) {
+    if (!A->w13_shared || !A->w2_shared) return MOE_ERR_NULL;
+    if (w_scaled(p->shared_w_dtype) && (!A->s13_shared || !A->s2_shared)) return MOE_ERR_NULL;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 moe_status_t moe_layer_workspace_size(const moe_problem_t* p, size_t* bytes) {
   moe_status_t st = check_problem(p, true, true);
   if (st != MOE_OK) return st;
@@ -664,15 +695,8 @@ moe_status_t moe_layer_workspace_size(const moe_problem_t* p, size_t* bytes) {
 
 moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* ws, size_t ws_bytes,
                        void* stream) {
-  moe_status_t st = check_problem(p, true, true);
+  moe_status_t st = check_layer_args(p, A);
   if (st != MOE_OK) return st;
-  if (!A || !A->x || !A->w13 || !A->w2 || !A->y) return MOE_ERR_NULL;
-  if (!A->logits_in && !A->w_router) return MOE_ERR_NULL;
-  if (w_scaled(p->w_dtype) && (!A->s13 || !A->s2)) return MOE_ERR_NULL;
-  if (p->I_shared) {
-    if (!A->w13_shared || !A->w2_shared) return MOE_ERR_NULL;
-    if (w_scaled(p->shared_w_dtype) && (!A->s13_shared || !A->s2_shared)) return MOE_ERR_NULL;
-  }
   const LayerLayout L = layer_layout(p);
   if (!ws) return MOE_ERR_NULL;
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -771,7 +795,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     S.out = h_sh;
     S.ldo = p->I_shared;
     S.rows = p->T;
-    S.m_slots = (p->T + pl.bm - 1) / pl.bm;
+    S.m_slots = static_cast<int32_t>((static_cast<int64_t>(p->T) + pl.bm - 1) / pl.bm);
   }
   {
     GSet& S = g1.s[si++];
@@ -809,7 +833,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
     S.n_out = p->D;
     S.out = o_sh;
     S.ldo = p->D;
-    S.m_slots = (p->T + pl2.bm - 1) / pl2.bm;
+    S.m_slots = static_cast<int32_t>((static_cast<int64_t>(p->T) + pl2.bm - 1) / pl2.bm);
   }
   {
     GSet& S = g2.s[si++];
@@ -944,8 +968,10 @@ extern "C" {
 size_t moe_layer_noalloc_max_bytes(void) { return kScratchBytes; }
 
 moe_status_t moe_layer_noalloc(const moe_problem_t* p, const moe_layer_args_t* A, void* stream) {
+  moe_status_t st = check_layer_args(p, A);   // before any HIP call
+  if (st != MOE_OK) return st;
   size_t need = 0;
-  moe_status_t st = moe_layer_workspace_size(p, &need);
+  st = moe_layer_workspace_size(p, &need);
   if (st != MOE_OK) return st;
   if (need > kScratchBytes) return MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);

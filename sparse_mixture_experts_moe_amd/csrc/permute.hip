@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict
 
 }  // namespace
 
-int perm_blocks(int T) { return (T + PB - 1) / PB; }
+int perm_blocks(int T) { return static_cast<int>((static_cast<int64_t>(T) + PB - 1) / PB); }
 
 int perm_small_max_tokens() { return 16 * 64; }
 
