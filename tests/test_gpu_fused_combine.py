@@ -113,3 +113,15 @@ def test_fused_combine_bit_exact_full_size(name):
     assert (n_sep, n_fus) == (1, 0), name
     del wl, sep, fus
     torch.cuda.empty_cache()
+
+
+def test_fused_combine_stable_over_many_calls():
+    """Twenty fused calls in a row on a layer whose tokens' rows come from
+    blocks on every XCD: each output equals the separate combine's bit for bit
+    (the owner's reads see every other block's rows each time)."""
+    cfg = shrink(CONFIGS["ling_decode"], T=384, D=1024, E=32, k=8, I=256, I_shared=256)
+    wl = to_device(generate(cfg, seed=14))
+    sep = run_layer(wl, combine="separate", want=())["y"]
+    for i in range(20):
+        fus = run_layer(wl, combine="fused", want=())["y"]
+        assert torch.equal(fus.view(torch.int16), sep.view(torch.int16)), f"call {i}"
