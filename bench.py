@@ -203,7 +203,7 @@ def main():
         copy_calib(args.copy_calib)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the layer runs on one GPU here; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
