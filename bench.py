@@ -52,8 +52,9 @@ def parse():
     ap.add_argument("--policy", default="auto", choices=["auto", "stream", "lds"])
     ap.add_argument("--combine", default="auto", choices=["auto", "separate", "fused"],
                     help="where the layer combines the expert rows (default: the library's choice)")
-    ap.add_argument("--act-quant", action="store_true",
-                    help="dynamic per-token fp8 activations in the expert GEMMs (fp8-weight workloads)")
+    ap.add_argument("--act-quant", nargs="?", const="row", default=None, choices=["row", "sub512"],
+                    help="dynamic fp8 activations in the expert GEMMs (fp8-weight workloads): one scale "
+                         "per token row (row, the default), or per 512-element sub-channel (sub512)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0)
     ap.add_argument("--copy-calib", type=int, default=0, metavar="MIB",
@@ -172,8 +173,11 @@ def cpu_baseline(wl, n_tokens: int, act_quant: int = 0):
         if sh is not None:
             shared = (*decode_weight(sh[0], sh[1], c.shared_w_dtype),
                       *decode_weight(sh[2], sh[3], c.shared_w_dtype))
-        fn = {0: layer, 1: layer_w8a8, 2: layer_w4a8}[act_quant]
-        fn(x, wr, c.k, expert, shared, c.act, c.act_shared)
+        if act_quant == 3:
+            layer_w8a8(x, wr, c.k, expert, shared, c.act, c.act_shared, width=512)
+        else:
+            fn = {0: layer, 1: layer_w8a8, 2: layer_w4a8}[act_quant]
+            fn(x, wr, c.k, expert, shared, c.act, c.act_shared)
 
     # whole passes over the sample until at least MIN_CPU_S seconds of work
     t0 = time.perf_counter()
@@ -191,7 +195,7 @@ def cpu_baseline(wl, n_tokens: int, act_quant: int = 0):
     model, affinity = cpu_identity()
     return {"value": passes * n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "cpu_model": model, "cpus_available": affinity,
-            "sample": (f"float64 NumPy oracle{['', ' (W8A8)', ' (W4A8)'][act_quant]}, whole layer on the "
+            "sample": (f"float64 NumPy oracle{['', ' (W8A8)', ' (W4A8)', ' (W8A8, 512-element sub-channels)'][act_quant]}, whole layer on the "
                        f"first {n_tokens} of {c.T} tokens "
                        f"({len(used)} experts decoded from {c.w_dtype} in each pass), "
                        f"{passes} pass{'es' if passes > 1 else ''}, {dt:.1f} s")}
@@ -221,7 +225,8 @@ def main():
     wl.x, wl.wr = wl.x.cuda(), wl.wr.cuda()
     # MXFP4 weights always run with MXFP8 activations (W4A8)
     aq = (B.MOE_ACT_QUANT_MXFP8 if cfg.w_dtype == "mxfp4"
-          else B.MOE_ACT_QUANT_FP8_ROW if args.act_quant else B.MOE_ACT_QUANT_NONE)
+          else B.MOE_ACT_QUANT_FP8_ROW if args.act_quant == "row"
+          else B.MOE_ACT_QUANT_FP8_SUB if args.act_quant == "sub512" else B.MOE_ACT_QUANT_NONE)
     p = B.make_problem(cfg.T, cfg.D, cfg.E, cfg.k, cfg.I, cfg.I_shared, cfg.act, cfg.act_shared,
                        cfg.act_dtype, cfg.w_dtype, cfg.shared_w_dtype, args.policy, act_quant=aq,
                        combine=args.combine)
@@ -293,7 +298,7 @@ def main():
     ridge = cm.PEAK_TFLOPS[wdt] * 1e12 / (cm.PEAK_HBM_GBS * 1e9)
     traffic = None
     tpath = os.path.join(ROOT, "profiles",
-                         f"traffic_{name}_{cfg.name}{'_w8a8' if aq == B.MOE_ACT_QUANT_FP8_ROW else ''}.json")
+                         f"traffic_{name}_{cfg.name}{ {1: '_w8a8', 3: '_w8a8sub'}.get(aq, '') }.json")
     if os.path.exists(tpath):
         tj = json.load(open(tpath))
         if tj.get("sources") and tj.get("sources_sha256") == sources_hash(tj["sources"]):
@@ -323,7 +328,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "D": cfg.D, "E": cfg.E, "k": cfg.k,
                    "I": cfg.I, "I_shared": cfg.I_shared, "act": cfg.act,
                    "w_dtype": cfg.w_dtype, "touched_experts": touched, "policy": args.policy,
-                   "act_quant": ["none", "fp8_per_token", "mxfp8"][aq]},
+                   "act_quant": ["none", "fp8_per_token", "mxfp8", "fp8_per_512_subchannel"][aq]},
         "roofline": roof,
         "grouped_gemm": {
             "ms_per_step": gemm_ms,

@@ -82,6 +82,8 @@ extern "C" {
 #define MOE_ACT_QUANT_NONE     0   /* bf16 activations                       */
 #define MOE_ACT_QUANT_FP8_ROW  1   /* dynamic per-token fp8 (see below)      */
 #define MOE_ACT_QUANT_MXFP8    2   /* dynamic MXFP8 blocks (see below)       */
+#define MOE_ACT_QUANT_FP8_SUB  3   /* dynamic fp8 per 512-column slice (below) */
+#define MOE_SUBCHANNEL       512   /* slice width of MOE_ACT_QUANT_FP8_SUB    */
 
 /* where moe_layer combines the expert rows (moe_problem_t.combine) */
 #define MOE_COMBINE_AUTO      0    /* the library's choice: separate (measured
@@ -149,6 +151,20 @@ typedef struct moe_problem {
  *                         Requires act BF16, MXFP4 routed and shared weights,
  *                         D, I and I_shared multiples of 128 and a tile policy
  *                         other than MOE_TILE_STREAM.
+ *  MOE_ACT_QUANT_FP8_SUB  as MOE_ACT_QUANT_FP8_ROW with one scale per
+ *                         MOE_SUBCHANNEL-column slice of each row instead of
+ *                         one per row: the 512 sub-channel activation
+ *                         quantisation of the fp8 grouped matmul on the "Qwen
+ *                         3.5 MoE on Ironwood" page (MoE track, GMM v2).  Each
+ *                         GEMM input row (x; the stored bf16 h) is quantised
+ *                         as moe_quantize_subchannel does; the row's sum is
+ *                         sum over slices j of s_j times the slice's fp8
+ *                         products (fp32 sums; the slice scale's power of two
+ *                         is applied by the matrix cores, its mantissa by
+ *                         rescaling the partial sums at each slice boundary),
+ *                         then scaled per output channel.  Requires what
+ *                         MOE_ACT_QUANT_FP8_ROW requires, with D, I and
+ *                         I_shared multiples of 512.
  */
 
 /*
@@ -332,6 +348,21 @@ moe_status_t moe_layer_noalloc(const moe_problem_t* p, const moe_layer_args_t* a
  */
 moe_status_t moe_quantize_rows(const void* a, int32_t rows, int32_t cols, int64_t lda, uint8_t* q,
                                float* scale, void* stream);
+
+/*
+ * moe_quantize_subchannel -- dynamic fp8 quantisation per 512-column slice
+ * (the sub-channel activation quantisation of the "Qwen 3.5 MoE on Ironwood"
+ * page, MoE track, GMM v2): moe_quantize_rows' rule applied to each slice of
+ * MOE_SUBCHANNEL consecutive columns of a row, with its own scale.
+ *   a     [rows, lda] bf16 (the first cols columns are read); lda % 8 == 0
+ *   q     [rows, cols] uint8 (written)
+ *   scale [cols / 512, rows] fp32 (written, slice-major: the scale of row r's
+ *         slice u at scale[u * rows + r])
+ *   cols % 512 == 0 and 0 < cols <= 16384, else MOE_ERR_SHAPE; a 16-byte and
+ *   q 8-byte aligned.  Non-finite inputs are outside the contract.
+ */
+moe_status_t moe_quantize_subchannel(const void* a, int32_t rows, int32_t cols, int64_t lda, uint8_t* q,
+                                     float* scale, void* stream);
 
 /*
  * moe_quantize_rows_mx -- dynamic MXFP8 quantisation, the activation side of

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 MOE_F32, MOE_BF16, MOE_FP8_E4M3FN, MOE_MXFP4_E2M1 = 0, 1, 2, 3
 MOE_ACT_SILU, MOE_ACT_GELU_TANH = 0, 1
 MOE_TILE_AUTO, MOE_TILE_STREAM, MOE_TILE_LDS = 0, 1, 2
-MOE_ACT_QUANT_NONE, MOE_ACT_QUANT_FP8_ROW, MOE_ACT_QUANT_MXFP8 = 0, 1, 2
+MOE_ACT_QUANT_NONE, MOE_ACT_QUANT_FP8_ROW, MOE_ACT_QUANT_MXFP8, MOE_ACT_QUANT_FP8_SUB = 0, 1, 2, 3
+MOE_SUBCHANNEL = 512
 MOE_COMBINE_AUTO, MOE_COMBINE_SEPARATE, MOE_COMBINE_FUSED = 0, 1, 2
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE = 0, 1, 2, 3
 MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH = 4, 5, 6
@@ -81,6 +82,7 @@ _SIG = {
     "moe_probe_mfma": [ctypes.c_int32, _vp, ctypes.c_int32, _vp, ctypes.POINTER(ctypes.c_double), _vp],
     "moe_quantize_rows": [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _vp, _vp, _vp],
     "moe_quantize_rows_mx": [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _vp, _vp, _vp],
+    "moe_quantize_subchannel": [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, _vp, _vp, _vp],
 }
 
 
@@ -245,6 +247,11 @@ def moe_quantize_rows(a, rows: int, cols: int, lda: int, q, scale, stream=None):
 def moe_quantize_rows_mx(a, rows: int, cols: int, lda: int, q, scale, stream=None):
     _check(lib().moe_quantize_rows_mx(_p(a), rows, cols, lda, _p(q), _p(scale), _stream(stream)),
            "moe_quantize_rows_mx")
+
+
+def moe_quantize_subchannel(a, rows: int, cols: int, lda: int, q, scale, stream=None):
+    _check(lib().moe_quantize_subchannel(_p(a), rows, cols, lda, _p(q), _p(scale), _stream(stream)),
+           "moe_quantize_subchannel")
 
 
 def moe_probe_hbm_read(buf, nbytes: int, sink, stream=None):

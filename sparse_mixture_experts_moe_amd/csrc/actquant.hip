@@ -10,6 +10,13 @@
 // to the even code, saturating at +-448), with both divisions correctly
 // rounded in fp32.
 //
+// The sub-channel variant (the GMM v2 kernel of the "Qwen 3.5 MoE on
+// Ironwood" page, MoE track: fp8 activations with one scale per 512-element
+// sub-channel) applies the same rule to each 512-element slice of a row; a
+// wavefront's register chunk u (64 lanes x 8 elements) is exactly slice u,
+// so each slice's max is one butterfly.  Its scales are stored slice-major,
+// [cols / 512][rows], the layout the GEMM's per-stage scale copies read.
+//
 // The MXFP8 variant is the activation side of the W4A8 decomposition ("CANN
 // Qwen3-MoE" page, high-throughput prefill), with the OCP microscaling block
 // format: per 32 elements an E8M0 scale 2^(floor(log2 amax) - 8), clamped to
@@ -21,6 +28,7 @@ namespace moe {
 namespace {
 
 constexpr int QMAX = 16384;           // widest row: 64 lanes x 32 chunks of 8
+static_assert(kSubChannel == 64 * 8, "a sub-channel slice is one chunk per lane");
 
 // e4m3fn code of v with |v| <= 448, from the format: sign, 4 exponent bits
 // (bias 7), 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9.
@@ -51,7 +59,8 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
 // One wavefront per row, 4 rows per block: lane l holds the row's 16-byte
 // chunks l, l + 64, ... (NCH of them) in registers between the max and the
 // conversion, so a row is read once and the reduction is a wavefront butterfly.
-template <int NCH>
+// SUB: one scale per 512-element slice (chunk group u), scale[u * rows + r].
+template <int NCH, bool SUB>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ a, int rows,
                                                          int cols, int64_t lda, uint8_t* __restrict__ q,
                                                          float* __restrict__ scale) {
@@ -66,24 +75,32 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
     const int c = lane + 64 * u;
     v[u] = c < nch ? *reinterpret_cast<const uint4*>(row + 8 * c) : uint4{0, 0, 0, 0};
   }
-  float amax = 0.f;
+  float amax[SUB ? NCH : 1];
+#pragma unroll
+  for (int u = 0; u < (SUB ? NCH : 1); ++u) amax[u] = 0.f;
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
     const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+    float& m = amax[SUB ? u : 0];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      amax = fmaxf(amax, fabsf(__uint_as_float(w[j] << 16)));
-      amax = fmaxf(amax, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
+      m = fmaxf(m, fabsf(__uint_as_float(w[j] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(w[j] & 0xFFFF0000u)));
     }
   }
+  float sc[SUB ? NCH : 1];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
-  const float s = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+  for (int u = 0; u < (SUB ? NCH : 1); ++u) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax[u] = fmaxf(amax[u], __shfl_xor(amax[u], off, 64));
+    sc[u] = amax[u] > 0.f ? __fdiv_rn(amax[u], 448.0f) : 1.0f;
+  }
   uint8_t* qrow = q + r * cols;
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
     const int c = lane + 64 * u;
     if (c >= nch) continue;
+    const float s = sc[SUB ? u : 0];
     const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
     uint32_t packed[2] = {0, 0};
 #pragma unroll
@@ -96,7 +113,15 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
     }
     *reinterpret_cast<uint2*>(qrow + 8 * c) = uint2{packed[0], packed[1]};
   }
-  if (lane == 0) scale[r] = s;
+  if (lane == 0) {
+    if constexpr (SUB) {
+#pragma unroll
+      for (int u = 0; u < NCH; ++u)
+        if (512 * u < cols) scale[static_cast<int64_t>(u) * rows + r] = sc[u];
+    } else {
+      scale[r] = sc[0];
+    }
+  }
 }
 
 // MXFP8: lane l's chunks l, l + 64, ...; the four chunks of a 32-element block
@@ -156,10 +181,10 @@ hipError_t go_mx(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q,
   return hipGetLastError();
 }
 
-template <int NCH>
+template <int NCH, bool SUB = false>
 hipError_t go(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q, float* scale,
               hipStream_t s) {
-  quant_rows_kernel<NCH><<<(rows + 3) / 4, 256, 0, s>>>(a, rows, cols, lda, q, scale);
+  quant_rows_kernel<NCH, SUB><<<(rows + 3) / 4, 256, 0, s>>>(a, rows, cols, lda, q, scale);
   return hipGetLastError();
 }
 
@@ -179,6 +204,21 @@ hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, int64_t lda,
   if (nch <= 8) return go<8>(a, rows, cols, lda, q, scale, s);
   if (nch <= 16) return go<16>(a, rows, cols, lda, q, scale, s);
   return go<32>(a, rows, cols, lda, q, scale, s);
+}
+
+hipError_t launch_quant_rows_sub(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q,
+                                 float* scale, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (rows < 0 || cols <= 0 || cols % kSubChannel || cols > QMAX || lda < cols || lda % 8)
+    return hipErrorInvalidValue;
+  if (reinterpret_cast<uintptr_t>(a) % 16 || reinterpret_cast<uintptr_t>(q) % 8) return hipErrorInvalidValue;
+  const int nch = cols / kSubChannel;     // chunks per lane = slices
+  if (nch <= 1) return go<1, true>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 2) return go<2, true>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 4) return go<4, true>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 8) return go<8, true>(a, rows, cols, lda, q, scale, s);
+  if (nch <= 16) return go<16, true>(a, rows, cols, lda, q, scale, s);
+  return go<32, true>(a, rows, cols, lda, q, scale, s);
 }
 
 hipError_t launch_quant_rows_mx(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q,

@@ -32,14 +32,17 @@ bool combo_ok(int act_dt, int w_dt) {
 bool quantised(const moe_problem_t* p) { return p->act_quant != MOE_ACT_QUANT_NONE; }
 
 // Bytes of the activation scales of `rows` quantised rows of `cols` columns:
-// one fp32 per row, or (MXFP8) one E8M0 byte per 32 columns.
+// one fp32 per row, (sub-channel) one fp32 per 512 columns, or (MXFP8) one
+// E8M0 byte per 32 columns.
 size_t qscale_bytes(const moe_problem_t* p, int64_t rows, int64_t cols) {
+  if (p->act_quant == MOE_ACT_QUANT_FP8_SUB) return static_cast<size_t>(rows * (cols / kSubChannel) * 4);
   return static_cast<size_t>(p->act_quant == MOE_ACT_QUANT_MXFP8 ? rows * (cols / 32) : rows * 4);
 }
 
 // Device dtype of the expert GEMMs' activations.
 int gemm_a_dtype(const moe_problem_t* p) {
   return p->act_quant == MOE_ACT_QUANT_FP8_ROW ? DT_FP8
+         : p->act_quant == MOE_ACT_QUANT_FP8_SUB ? DT_FP8S
          : p->act_quant == MOE_ACT_QUANT_MXFP8 ? DT_MXFP8 : p->act_dtype;
 }
 
@@ -49,18 +52,28 @@ hipError_t quant_rows(const moe_problem_t* p, const void* a, int rows, int cols,
   if (p->act_quant == MOE_ACT_QUANT_MXFP8)
     return launch_quant_rows_mx(static_cast<const uint16_t*>(a), rows, cols, cols, q,
                                 static_cast<uint8_t*>(scale), s);
+  if (p->act_quant == MOE_ACT_QUANT_FP8_SUB)
+    return launch_quant_rows_sub(static_cast<const uint16_t*>(a), rows, cols, cols, q,
+                                 static_cast<float*>(scale), s);
   return launch_quant_rows(static_cast<const uint16_t*>(a), rows, cols, cols, q,
                            static_cast<float*>(scale), s);
 }
 
-// Point a GEMM set's activation and weight scales at the right buffers.
+// Point a GEMM set's activation and weight scales at the right buffers (S.K
+// set first: the sub-channel scales' last slice is the epilogue's).
 void set_scales(const moe_problem_t* p, GSet& S, const void* a_scale, int32_t a_scale_rows,
                 const void* w_scale, int w_dtype, int64_t w_scale_gstride_bytes) {
   S.a_scale = nullptr;
   S.a_mx = nullptr;
   S.w_mx = nullptr;
   S.scale = nullptr;
+  S.a_sub = nullptr;
   if (p->act_quant == MOE_ACT_QUANT_FP8_ROW) S.a_scale = static_cast<const float*>(a_scale);
+  if (p->act_quant == MOE_ACT_QUANT_FP8_SUB) {
+    S.a_sub = static_cast<const float*>(a_scale);
+    S.a_sub_rows = a_scale_rows;
+    S.a_scale = S.a_sub + static_cast<int64_t>(S.K / kSubChannel - 1) * a_scale_rows;
+  }
   if (p->act_quant == MOE_ACT_QUANT_MXFP8) {
     S.a_mx = static_cast<const uint8_t*>(a_scale);
     S.a_mx_rows = a_scale_rows;
@@ -102,7 +115,7 @@ moe_status_t check_problem(const moe_problem_t* p, bool need_ffn, bool need_rout
   if (need_ffn && p->I_shared && !combo_ok(p->act_dtype, p->shared_w_dtype))
     return MOE_ERR_UNSUPPORTED;
   if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_UNSUPPORTED;
-  if (p->act_quant < MOE_ACT_QUANT_NONE || p->act_quant > MOE_ACT_QUANT_MXFP8) return MOE_ERR_UNSUPPORTED;
+  if (p->act_quant < MOE_ACT_QUANT_NONE || p->act_quant > MOE_ACT_QUANT_FP8_SUB) return MOE_ERR_UNSUPPORTED;
   if (p->combine < MOE_COMBINE_AUTO || p->combine > MOE_COMBINE_FUSED) return MOE_ERR_UNSUPPORTED;
   // MXFP4 weights go with MXFP8 activations and nothing else, on both branches
   const bool mx = p->act_quant == MOE_ACT_QUANT_MXFP8;
@@ -116,7 +129,7 @@ moe_status_t check_problem(const moe_problem_t* p, bool need_ffn, bool need_rout
     if (p->act_dtype != MOE_BF16 || p->w_dtype != wdt) return MOE_ERR_UNSUPPORTED;
     if (p->I_shared && p->shared_w_dtype != wdt) return MOE_ERR_UNSUPPORTED;
     if (p->tile_policy == MOE_TILE_STREAM) return MOE_ERR_UNSUPPORTED;
-    const int km = tiled_k_multiple_a8();
+    const int km = p->act_quant == MOE_ACT_QUANT_FP8_SUB ? kSubChannel : tiled_k_multiple_a8();
     if (p->D % km || p->I % km || p->I_shared % km) return MOE_ERR_UNSUPPORTED;
     const int qm = quant_max_cols();
     if (p->D > qm || p->I > qm || p->I_shared > qm) return MOE_ERR_UNSUPPORTED;
@@ -162,9 +175,11 @@ bool tiled_fits(const moe_problem_t* p) {
 
 Plan make_plan(const moe_problem_t* p, double mean_rows) {
   if (quantised(p)) {
-    // fp8 x fp8, MXFP8 x MXFP4: the tiled kernel's quantised shapes
+    // fp8 x fp8, MXFP8 x MXFP4: the tiled kernel's quantised shapes (with
+    // sub-channel scales, no 128 x 512 tiles)
+    const bool wide_ok = p->act_quant != MOE_ACT_QUANT_FP8_SUB;
     const int shape = mean_rows <= kSmallMax ? TILED_SMALLQ
-                      : mean_rows <= kTallMean ? TILED_TALL : TILED_WIDE;
+                      : (mean_rows <= kTallMean || !wide_ok) ? TILED_TALL : TILED_WIDE;
     return Plan{true, 0, tiled_bm(shape), shape};
   }
   const bool tiled_ok = kTiledReady && p->act_dtype == MOE_BF16 && tiled_fits(p);
@@ -1008,6 +1023,19 @@ moe_status_t moe_quantize_rows_mx(const void* a, int32_t rows, int32_t cols, int
   hipStream_t s = static_cast<hipStream_t>(stream);
   StageScope sc(ST_QUANT, s);
   MOE_LAUNCH(launch_quant_rows_mx(static_cast<const uint16_t*>(a), rows, cols, lda, q, scale, s));
+  return MOE_OK;
+}
+
+moe_status_t moe_quantize_subchannel(const void* a, int32_t rows, int32_t cols, int64_t lda, uint8_t* q,
+                                     float* scale, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % kSubChannel || cols > quant_max_cols() || lda < cols || lda % 8)
+    return MOE_ERR_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!a || !q || !scale) return MOE_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(a) % 16 || reinterpret_cast<uintptr_t>(q) % 8) return MOE_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StageScope sc(ST_QUANT, s);
+  MOE_LAUNCH(launch_quant_rows_sub(static_cast<const uint16_t*>(a), rows, cols, lda, q, scale, s));
   return MOE_OK;
 }
 

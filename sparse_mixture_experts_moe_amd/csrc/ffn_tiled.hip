@@ -84,10 +84,11 @@ constexpr int BK8A = 128;                 // stage depth of fp8 x fp8 tiles (64 
 constexpr int LDS_CU = 160 * 1024;        // LDS per CU
 
 template <int BM_, int BNW_, int WM_, int WN_, int BPC_, bool FP8, int BK_, int MF_, bool A8_ = false,
-          bool W4_ = false>
+          bool W4_ = false, bool SUB_ = false>
 struct Cfg {
   static constexpr bool A8 = A8_;                     // fp8 activations (with fp8 weights)
   static constexpr bool W4 = W4_;                     // MXFP4 weights, MXFP8 activations (with A8)
+  static constexpr bool SUB = SUB_;                   // fp8 activations with sub-channel scales (with A8)
   static constexpr bool W8 = FP8;                     // one-byte weights (fp8, or e2m1 pairs with W4)
   static constexpr int MF = MF_;                      // MFMA tile: 16 (16x16x32) or 32 (32x32x16 / x64 fp8)
   static constexpr int BK = BK_;                      // K elements per stage
@@ -110,8 +111,9 @@ struct Cfg {
   static constexpr int B_BYTES = BNW * ROWBW;
   // MX block scales of a stage, 4 bytes per row ([row][block]): activation
   // rows one 4-byte copy per lane (gathered rows), weight rows 16 bytes (four
-  // consecutive rows) per lane
-  static constexpr int ASC_BYTES = W4 ? BM * 4 : 0;
+  // consecutive rows) per lane.  Sub-channel scales: the fp32 scale of the
+  // stage's slice for each activation row, copied the same way.
+  static constexpr int ASC_BYTES = (W4 || SUB) ? BM * 4 : 0;
   static constexpr int BSC_BYTES = W4 ? BNW * 4 : 0;
   static constexpr int ASC_I = ASC_BYTES / 256, BSC_I = BSC_BYTES / 1024;
   static constexpr int NSC = ASC_I + BSC_I;           // scale copy instructions (one per wavefront)
@@ -130,6 +132,7 @@ struct Cfg {
   static_assert(WPE == 1 || WPE == 2, "one or two wavefronts per SIMD");
   static_assert(!A8 || (FP8 && MF == 32), "fp8 activations: fp8 weights, 32x32x64 MFMAs");
   static_assert(!W4 || (A8 && BK == 128), "MX weights: fp8 activations, 128-deep stages");
+  static_assert(!SUB || (A8 && !W4 && kSubChannel % BK == 0), "sub-channel scales: whole stages per slice");
   static_assert(ASC_I * 256 == ASC_BYTES && BSC_I * 1024 == BSC_BYTES && NSC <= NW, "scale copies");
 };
 
@@ -180,6 +183,17 @@ template <class T> __device__ __forceinline__ T* uniform_ptr(T* p) {
 
 // Wait until at most N of this wavefront's vector-memory operations are in
 // flight (they complete in order).
+// A sub-channel scale s > 0 as m 2^(e - 127): e the E8M0 code of s's power of
+// two (floor(log2 s) kept within [-127, 127]) and m = s / 2^(e - 127), in
+// [1, 2) for a normal s; both parts exact.
+__device__ __forceinline__ float split_scale(float s, int& e) {
+  int ex;
+  (void)frexpf(s, &ex);            // s = f 2^ex, f in [0.5, 1)
+  const int p = min(127, max(-127, ex - 1));
+  e = p + 127;
+  return ldexpf(s, -p);
+}
+
 template <int N> __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
@@ -357,8 +371,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   // An (empty) statement that names an accumulation register makes the backend
   // select the AGPR form of the MFMAs, so the accumulators live in AGPRs and
-  // the VGPRs stay free for fragments.
-  asm volatile("" ::: "a0");
+  // the VGPRs stay free for fragments.  The sub-channel kernels rescale their
+  // accumulators with vector multiplies, so theirs stay in VGPRs (in AGPRs
+  // the rescale spilled).
+  if constexpr (!C::SUB) asm volatile("" ::: "a0");
   int b = blockIdx.x;
   if constexpr (xcdtile<C>())
     if (xcdtile_ok(g) && !xcdtile_block<C>(g, blockIdx.x, b)) return;
@@ -486,20 +502,37 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
       sc_base = uniform_ptr(reinterpret_cast<const char*>(Sg.w_mx) + group * Sg.w_mx_gstride + kg0 * sc_stride);
     }
   }
+  if constexpr (C::SUB) {
+    // wavefront w < ASC_I copies the scales of tile rows [64 w, 64 w + 64)
+    // for the stage's slice ([slice][row] fp32, gathered rows)
+    if (wave < C::ASC_I) {
+      const int r = row0 + 64 * wave + lane;
+      int64_t arow = 0;
+      if (r < row1) {
+        arow = Sg.gather ? Sg.gather[r] : r;
+        if (static_cast<uint64_t>(arow) >= static_cast<uint64_t>(Sg.a_rows)) arow = 0;
+      }
+      sc_off = static_cast<uint32_t>(arow * 4);
+      sc_stride = static_cast<int64_t>(Sg.a_sub_rows) * 4;
+      sc_base = uniform_ptr(reinterpret_cast<const char*>(Sg.a_sub) + (k_beg / kSubChannel) * sc_stride);
+    }
+  }
   auto issue_scales = [&](int st) __attribute__((always_inline)) {
+    char* sc_lds = smem + (st % S) * C::STAGE + C::A_BYTES + C::B_BYTES;
     if constexpr (C::W4) {
-      char* sc_lds = smem + (st % S) * C::STAGE + C::A_BYTES + C::B_BYTES;
       if (wave < C::ASC_I)
         dma4(sc_off, sc_base + st * sc_stride, sc_lds + wave * 256);
       else if (wave < C::NSC)
         dma16(sc_off, sc_base + st * sc_stride, sc_lds + C::ASC_BYTES + (wave - C::ASC_I) * 1024);
+    } else if constexpr (C::SUB) {
+      if (wave < C::ASC_I) dma4(sc_off, sc_base + (st / (kSubChannel / C::BK)) * sc_stride, sc_lds + wave * 256);
     }
   };
   // Waits for copies: this wavefront issues P copies per stage, plus one scale
   // copy if it is a scale copier.
   auto wait_stages = [&](int newer, auto m) __attribute__((always_inline)) {
     constexpr int M = decltype(m)::value;
-    if constexpr (C::W4) {
+    if constexpr (C::W4 || C::SUB) {
       if (wave < C::NSC) wait_newer<P + 1, M>(newer);
       else wait_newer<P, M>(newer);
     } else {
@@ -544,7 +577,16 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
     int sa[TF];
     int sb[WF];
   };
-  using Frag = typename std::conditional<C::W4, Frag4, typename std::conditional<A8, Frag8, FragW>::type>::type;
+  struct Frag8S {    // fp8 activations with their rows' slice scales s = m 2^(e - 127)
+    i32x8 a[TF];
+    i32x8 b[WF];
+    float s[TF];
+    int e[TF];
+    float m[TF];
+  };
+  using Frag = typename std::conditional<
+      C::W4, Frag4,
+      typename std::conditional<A8, typename std::conditional<C::SUB, Frag8S, Frag8>::type, FragW>::type>::type;
   // 16-byte chunk (of the tile row) holding the lane's K elements of sub-step
   // h of a stage, in MFMA ks
   auto chunk_of = [&](int h, int ks) __attribute__((always_inline)) -> int {
@@ -597,6 +639,12 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
       for (int i = 0; i < TF; ++i) F.a[i] = rd(base, wm * TF * MF + MF * i + lr);
 #pragma unroll
       for (int f = 0; f < WF; ++f) F.b[f] = rd(bb, wrow_of(f));
+      if constexpr (C::SUB) {
+        const char* asc = bb + C::B_BYTES;
+#pragma unroll
+        for (int i = 0; i < TF; ++i)
+          F.s[i] = *reinterpret_cast<const float*>(asc + 4 * (wm * TF * MF + MF * i + lr));
+      }
       return;
     } else {
 #pragma unroll
@@ -642,6 +690,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
 #pragma unroll
       for (int f = 0; f < WF; ++f) asm volatile("" ::"v"(F.b[f]));
 #endif
+      if constexpr (C::SUB) {
+#pragma unroll
+        for (int i = 0; i < TF; ++i) F.m[i] = split_scale(F.s[i], F.e[i]);
+      }
       return;
     } else {
 #pragma unroll
@@ -659,6 +711,33 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
         if constexpr (MF == 32) F.w[f][1] = fp8x8_to_bf16x8(F.b[f][0][2], F.b[f][0][3]);
       }
     }
+    }
+  };
+  // Sub-channel scales (the "Qwen 3.5 MoE on Ironwood" page, MoE track, GMM
+  // v2: fp8 activations with one scale per 512-element slice).  A row's sum
+  // is sum_j s_j P_j over its slices j, s_j = m_j 2^e_j.  The matrix cores
+  // apply 2^e_j as the activation block scale; the accumulators hold the sum
+  // in units of the current slice's mantissa, so at each slice's first
+  // sub-step they are multiplied by m_(j-1) / m_j (between 1/2 and 2: no
+  // overflow, one rounding), and the epilogue multiplies by the last m.
+  [[maybe_unused]] float mprev[C::SUB ? TF : 1];
+  auto rescale = [&](const Frag& F, int t) __attribute__((always_inline)) {
+    if constexpr (C::SUB) {
+      constexpr int SPS = kSubChannel / C::KSUB;   // sub-steps per slice
+      if (t % SPS == 0) {
+        if (t > 0) {
+#pragma unroll
+          for (int i = 0; i < TF; ++i) {
+            const float r = mprev[i] / F.m[i];
+#pragma unroll
+            for (int f = 0; f < WF; ++f)
+#pragma unroll
+              for (int e = 0; e < MF * MF / 64; ++e) acc[f][i][e] *= r;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < TF; ++i) mprev[i] = F.m[i];
+      }
     }
   };
   // MFMAs of one sub-step, row fragment by row fragment; fragments past the
@@ -679,6 +758,11 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
                              static_cast<int>(w[3]), 0, 0, 0, 0};
               acc[f][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w8, F.a[i], acc[f][i], 4, 0, 0,
                                                                           F.sb[f], 0, F.sa[i]);
+            } else if constexpr (C::SUB) {
+              // e4m3 x e4m3, the activation rows' slice scales' powers of two
+              // as their block scales (the mantissas are applied outside)
+              acc[f][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[f], F.a[i], acc[f][i], 0, 0,
+                                                                          0, 127, 0, F.e[i]);
             } else if constexpr (A8) {
               // e4m3 x e4m3 (format codes 0), unit block scales (exponent 127)
               acc[f][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(F.b[f], F.a[i], acc[f][i], 0, 0,
@@ -726,12 +810,14 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
         issue_chunk(x + S, std::integral_constant<int, 0>());
       }
       readf(nxt, t + 1);   // t + 1 == nst * H reads a stale slot that is never used
+      rescale(cur, t);
       mma(cur);
     } else {
       const int x = t / H - 1;         // its slot was freed by the last barrier
       settle(cur);                     // (decodes fp8 weights)
       if (x >= 0 && x + S < nst) issue_chunk(x + S, std::integral_constant<int, PH + 1>());
       readf(nxt, t + 1);
+      rescale(cur, t);
       mma(cur);
     }
   };
@@ -814,6 +900,10 @@ __global__ __launch_bounds__(C::THREADS, C::WPE) void tiled_gemm_kernel(const GA
       if (r >= row1 || !col_ok) continue;
       float ra = 1.f;   // the row's activation scale (fp8 activations)
       if constexpr (A8 && !C::W4) ra = Sg.a_scale[Sg.gather ? Sg.gather[r] : r];
+      if constexpr (C::SUB) {
+        int e_unused;
+        ra = split_scale(ra, e_unused);   // the last slice's mantissa (its power of two is in the sums)
+      }
       float v[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -901,6 +991,17 @@ hipError_t dispatch(const GArgs& g, bool gated, int w_dtype, int out_dtype, int 
     }
     return hipErrorInvalidValue;
   }
+  if (a_dtype == DT_FP8S) {
+    // fp8 x fp8 with sub-channel activation scales: 64-deep stages, so that
+    // the stage's scale row fits beside the ring; 256-row tiles only (the
+    // 128 x 512 block's registers do not hold the rescaled accumulators)
+    if constexpr (BPC == 1 && BM == 256) {
+      using CS = Cfg<BM, BNW, WM, WN, 1, true, 64, 32, true, false, true>;
+      if (w_dtype != DT_FP8 || out_dtype != DT_BF16) return hipErrorInvalidValue;
+      return gated ? launch_one<CS, true, DT_FP8, DT_BF16>(g, s) : launch_one<CS, false, DT_FP8, DT_BF16>(g, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (gated) {
     if (w_dtype == DT_BF16 && out_dtype == DT_BF16) return launch_one<CB, true, DT_BF16, DT_BF16>(g, s);
     if (w_dtype == DT_FP8 && out_dtype == DT_BF16) return launch_one<C8, true, DT_FP8, DT_BF16>(g, s);
@@ -952,9 +1053,12 @@ hipError_t dispatch_smallq(const GArgs& g, bool gated, int w_dtype, int out_dtyp
                            hipStream_t s) {
   using CA = Cfg<64, 256, 1, 4, 2, true, 128, 32, true>;
   using CW = Cfg<64, 256, 1, 4, 2, true, 128, 32, true, true>;
+  using CS = Cfg<64, 256, 1, 4, 2, true, 64, 32, true, false, true>;
   if (out_dtype != DT_BF16) return hipErrorInvalidValue;
   if (a_dtype == DT_FP8 && w_dtype == DT_FP8)
     return gated ? launch_one<CA, true, DT_FP8, DT_BF16>(g, s) : launch_one<CA, false, DT_FP8, DT_BF16>(g, s);
+  if (a_dtype == DT_FP8S && w_dtype == DT_FP8)
+    return gated ? launch_one<CS, true, DT_FP8, DT_BF16>(g, s) : launch_one<CS, false, DT_FP8, DT_BF16>(g, s);
   if (a_dtype == DT_MXFP8 && w_dtype == DT_MXFP4)
     return gated ? launch_one<CW, true, DT_MXFP4, DT_BF16>(g, s) : launch_one<CW, false, DT_MXFP4, DT_BF16>(g, s);
   return hipErrorInvalidValue;
@@ -996,6 +1100,8 @@ hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype,
     const int ks = S.ksplit > 1 ? S.ksplit : 1;
     if ((S.K / ks) % (2 * KS) || S.bm != tiled_bm(shape) || S.n_out % 4) return hipErrorInvalidValue;
     if (a_dtype == DT_FP8 && ((S.K / ks) % tiled_k_multiple_a8() || !S.a_scale)) return hipErrorInvalidValue;
+    if (a_dtype == DT_FP8S && (ks != 1 || S.K % kSubChannel || !S.a_scale || !S.a_sub || S.a_sub_rows < S.a_rows))
+      return hipErrorInvalidValue;
     if (a_dtype == DT_MXFP8 && ((S.K / ks) % tiled_k_multiple_a8() || !S.a_mx || !S.w_mx ||
                                 S.a_mx_rows < S.a_rows || S.NB % 4))
       return hipErrorInvalidValue;

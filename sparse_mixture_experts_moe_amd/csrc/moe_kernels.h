@@ -8,8 +8,11 @@ namespace moe {
 
 // ------------------------------------------------------------------ dtypes
 // DT_MXFP4: e2m1 pairs per byte (element 2j in the low nibble) with E8M0
-// block scales; DT_MXFP8: e4m3fn codes with E8M0 block scales (activations)
-enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3, DT_MXFP8 = 4 };
+// block scales; DT_MXFP8: e4m3fn codes with E8M0 block scales (activations);
+// DT_FP8S: e4m3fn codes with one fp32 scale per kSubChannel-element slice of
+// a row (activations)
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2, DT_MXFP4 = 3, DT_MXFP8 = 4, DT_FP8S = 5 };
+constexpr int kSubChannel = 512;
 enum : int { ACT_SILU = 0, ACT_GELU_TANH = 1 };
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -51,6 +54,10 @@ struct GSet {
   int32_t a_mx_rows;
   const uint8_t* w_mx;
   int64_t w_mx_gstride;     // bytes between groups' weight scales
+  // sub-channel scales of fp8 A rows (DT_FP8S): [K / kSubChannel][a_sub_rows]
+  // fp32 (storage rows); a_scale then points at the last slice's row of them
+  const float* a_sub;
+  int32_t a_sub_rows;
   const void* w;            // [groups][NB][K] weight storage
   const float* scale;       // [groups][NB] per-output-channel scales or null
   int64_t w_gstride;        // elements between groups (NB*K)
@@ -218,7 +225,9 @@ int stream_max_mt(int a_dtype);              // largest mt the stream kernel run
 // Every set's bm must be tiled_bm(shape).
 enum : int { TILED_TALL = 0, TILED_WIDE = 1, TILED_NARROW = 2, TILED_SMALL = 3, TILED_SMALLQ = 4 };
 // a_dtype DT_FP8 (fp8 activations with fp8 weights, bf16 output, one block
-// per CU shapes only) needs every set's a_scale; a_dtype DT_MXFP8 (with
+// per CU shapes only) needs every set's a_scale; DT_FP8S (the same with
+// sub-channel scales, K a multiple of kSubChannel, no K slices) every set's
+// a_sub, a_sub_rows >= a_rows, and a_scale at the last slice; a_dtype DT_MXFP8 (with
 // DT_MXFP4 weights, same shapes and output) every set's a_mx and w_mx, with
 // a_mx_rows >= a_rows.
 hipError_t launch_tiled_gemm(const GArgs& g, int shape, bool gated, int w_dtype, int out_dtype,
@@ -237,6 +246,10 @@ bool tiled_offsets_fit(int64_t a_rows, int64_t lda, int64_t w_rows, int64_t K, i
 int quant_max_cols();
 hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q,
                              float* scale, hipStream_t s);
+// The same per kSubChannel-element slice of each row: scale[u * rows + r] for
+// slice u.  cols % kSubChannel == 0, cols <= quant_max_cols().
+hipError_t launch_quant_rows_sub(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q,
+                                 float* scale, hipStream_t s);
 // MXFP8 quantisation of bf16 rows: per block of 32 elements an E8M0 scale
 // 2^(floor(log2 amax) - 8) (clamped to [2^-127, 2^127]; 2^-127 for a zero
 // block) and e4m3fn codes of a / scale (nearest even, saturating).  Scales go

@@ -159,6 +159,54 @@ def test_quantize_rows_mx_validation(lib):
     assert f(None, 0, 128, 128, None, None, None) == B.MOE_OK
 
 
+def _sub_problem(**over):
+    p = B.make_problem(64, 1024, 8, 2, 512, 512, act_dtype="bf16", w_dtype="fp8",
+                       act_quant=B.MOE_ACT_QUANT_FP8_SUB)
+    for k, v in over.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(), B.MOE_OK), (dict(I_shared=0), B.MOE_OK),
+    (dict(D=768), B.MOE_ERR_UNSUPPORTED), (dict(I=256), B.MOE_ERR_UNSUPPORTED),   # K multiple of 512
+    (dict(I_shared=1536), B.MOE_OK), (dict(I_shared=640), B.MOE_ERR_UNSUPPORTED),
+    (dict(w_dtype=B.MOE_BF16, shared_w_dtype=B.MOE_BF16), B.MOE_ERR_UNSUPPORTED),
+    (dict(tile_policy=B.MOE_TILE_STREAM), B.MOE_ERR_UNSUPPORTED),
+    (dict(act_quant=4), B.MOE_ERR_UNSUPPORTED),
+])
+def test_subchannel_validation(lib, over, status):
+    p = _sub_problem(**over)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_layer_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+    assert lib.moe_grouped_ffn_workspace_size(ctypes.byref(p), 8, 128, ctypes.byref(n)) == status
+
+
+def test_subchannel_workspace_holds_the_slice_scales(lib):
+    """The fp8 copies of x, h and h_shared take one byte per element plus one
+    fp32 scale per 512 elements."""
+    p, p0 = _sub_problem(T=1000), _sub_problem(T=1000)
+    p0.act_quant = 0
+    T, D, k, I, Is = 1000, 1024, 2, 512, 512
+    extra = B.moe_layer_workspace_size(p) - B.moe_layer_workspace_size(p0)
+    want = (T * D + T * k * I + T * Is) * (1 + 4 / 512)
+    assert want <= extra <= want + 6 * 256
+
+
+def test_quantize_subchannel_validation(lib):
+    fake = 4096
+    f = lib.moe_quantize_subchannel
+    assert f(fake, 4, 256, 256, fake, fake, None) == B.MOE_ERR_SHAPE      # cols % 512
+    assert f(fake, 4, 1024, 512, fake, fake, None) == B.MOE_ERR_SHAPE     # lda < cols
+    assert f(fake, 4, 512, 516, fake, fake, None) == B.MOE_ERR_SHAPE      # lda % 8
+    assert f(fake, 4, 1 << 15, 1 << 15, fake, fake, None) == B.MOE_ERR_SHAPE
+    assert f(fake, -1, 512, 512, fake, fake, None) == B.MOE_ERR_SHAPE
+    assert f(fake + 8, 4, 512, 512, fake, fake, None) == B.MOE_ERR_SHAPE   # a 16-byte aligned
+    assert f(None, 4, 512, 512, fake, fake, None) == B.MOE_ERR_NULL
+    assert f(fake, 4, 512, 512, fake, None, None) == B.MOE_ERR_NULL
+    assert f(None, 0, 512, 512, None, None, None) == B.MOE_OK
+
+
 def test_quantize_rows_validation(lib):
     fake = 4096
     assert lib.moe_quantize_rows(fake, 4, 12, 16, fake, fake, None) == B.MOE_ERR_SHAPE   # cols % 8
