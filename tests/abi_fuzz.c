@@ -52,9 +52,9 @@ static int valid_status(moe_status_t st) { return st >= MOE_OK && st <= MOE_ERR_
  * value from a wider set that includes unsupported and invalid ones. */
 static moe_problem_t random_problem(void) {
   static const int32_t Ts[] = {0, 1, 7, 64, 300, 512, 4097, 16384, 36000, 200000};
-  static const int32_t Ds[] = {64, 128, 192, 256, 512, 2816, 4096, 8192, 16384};
+  static const int32_t Ds[] = {64, 128, 192, 256, 512, 1024, 2816, 4096, 8192, 16384};
   static const int32_t Es[] = {1, 3, 8, 10, 16, 64, 128, 256, 512, 1024};
-  static const int32_t Is[] = {64, 128, 192, 256, 704, 1024, 2048};
+  static const int32_t Is[] = {64, 128, 192, 256, 512, 704, 1024, 2048};
   static const int32_t Iss[] = {0, 64, 128, 256, 1024, 2048, 2112};
   static const int32_t wds[] = {MOE_BF16, MOE_FP8_E4M3FN, MOE_MXFP4_E2M1};
   static const int32_t wide_T[] = {-3, 0, 1, 1 << 22, 1 << 29, 0x7fffffff};
@@ -83,8 +83,9 @@ static moe_problem_t random_problem(void) {
   }
   p.tile_policy = (int32_t)(next_u32() % 3);
   p.act_quant = p.w_dtype == MOE_MXFP4_E2M1 ? MOE_ACT_QUANT_MXFP8
-                : (p.w_dtype == MOE_FP8_E4M3FN && next_u32() % 2) ? MOE_ACT_QUANT_FP8_ROW
-                                                                   : MOE_ACT_QUANT_NONE;
+                : (p.w_dtype == MOE_FP8_E4M3FN && next_u32() % 2)
+                    ? ((next_u32() % 2) ? MOE_ACT_QUANT_FP8_ROW : MOE_ACT_QUANT_FP8_SUB)
+                    : MOE_ACT_QUANT_NONE;
   p.combine = (int32_t)(next_u32() % 3);
   if (next_u32() % 3 == 0) {
     switch (next_u32() % 12) {
@@ -156,7 +157,9 @@ int main(void) {
     int64_t lda = (int64_t)cols + (int64_t)(next_u32() % 64) - 16;
     moe_status_t s1 = moe_quantize_rows(NULL, rows, cols, lda, NULL, NULL, NULL);
     moe_status_t s2 = moe_quantize_rows_mx(NULL, rows, cols, lda, NULL, NULL, NULL);
-    CHECK(valid_status(s1) && valid_status(s2), "quantiser status %d %d", (int)s1, (int)s2);
+    moe_status_t s3 = moe_quantize_subchannel(NULL, rows, cols, lda, NULL, NULL, NULL);
+    CHECK(valid_status(s1) && valid_status(s2) && valid_status(s3), "quantiser status %d %d %d", (int)s1,
+          (int)s2, (int)s3);
     CHECK(rows != 0 || s1 != MOE_ERR_NULL, "zero rows need no pointers");
   }
   /* names of every value */
