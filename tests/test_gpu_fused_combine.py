@@ -29,6 +29,10 @@ QUANT = {
                     B.MOE_ACT_QUANT_FP8_ROW),
     "w4a8_wide": (shrink(CONFIGS["ling_prefill_mxfp4"], T=700, D=512, E=4, k=2, I=256, I_shared=128),
                   B.MOE_ACT_QUANT_MXFP8),
+    "w8a8_sub_tall": (shrink(CONFIGS["ling_prefill"], T=700, D=1024, E=4, k=2, I=512, I_shared=512),
+                      B.MOE_ACT_QUANT_FP8_SUB),
+    "w8a8_sub_decode": (shrink(CONFIGS["ling_decode"], T=96, D=1024, E=32, k=4, I=512, I_shared=512),
+                        B.MOE_ACT_QUANT_FP8_SUB),
 }
 
 
