@@ -24,22 +24,28 @@ CFGS = {
     "prefill": shrink(CONFIGS["qwen_prefill"], T=1200, D=256, E=64, k=8, I=128, I_shared=128),
     # fp8 weights
     "fp8": shrink(CONFIGS["ling_decode"], T=200, D=256, E=16, k=4, I=128, I_shared=128),
+    # fp8 activations per 512-element sub-channel (quantiser launches, scale copies)
+    "w8a8_sub": shrink(CONFIGS["ling_prefill"], T=700, D=1024, E=4, k=2, I=512, I_shared=512),
 }
+# modes of the graph cases: (act_quant, combine)
+MODES = {"decode": (0, "auto"), "prefill": (0, "auto"), "fp8": (0, "auto"),
+         "w8a8_sub": (B.MOE_ACT_QUANT_FP8_SUB, "auto"), "fused": (0, "fused")}
+CFGS_OF = {"fused": "fp8"}
 
 
 def _bits(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-def _call(wl, ws, y, stream=None):
-    p = problem(wl.cfg)
+def _call(wl, ws, y, stream=None, mode=(0, "auto")):
+    p = problem(wl.cfg, act_quant=mode[0], combine=mode[1])
     B.run_layer(p, wl.x, wl.w13, wl.w2, w_router=wl.wr, s13=wl.s13, s2=wl.s2,
                 w13_shared=wl.w13s, s13_shared=wl.s13s, w2_shared=wl.w2s, s2_shared=wl.s2s,
                 ws=ws, y=y, stream=stream)
 
 
-def _buffers(wl):
-    need = B.moe_layer_workspace_size(problem(wl.cfg))
+def _buffers(wl, mode=(0, "auto")):
+    need = B.moe_layer_workspace_size(problem(wl.cfg, act_quant=mode[0], combine=mode[1]))
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
     y = torch.empty((wl.cfg.T, wl.cfg.D), dtype=wl.x.dtype, device="cuda")
     return ws, y
@@ -70,17 +76,18 @@ def test_layers_on_two_streams_at_once():
             assert torch.equal(_bits(bufs[2 * i + rep][1]), _bits(alone[i])), (i, rep)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "prefill", "w8a8_sub", "fused"])
 def test_layer_in_a_captured_graph(name):
-    cfg = CFGS[name]
+    cfg = CFGS[CFGS_OF.get(name, name)]
+    mode = MODES[name]
     wl = to_device(generate(cfg, seed=12))
     xs = [wl.x.clone()] + [torch.randn_like(wl.x, dtype=torch.float32).to(wl.x.dtype) for _ in range(3)]
-    ws, y = _buffers(wl)
+    ws, y = _buffers(wl, mode)
     # eager results for every input (this also loads the kernels before capture)
     want = []
     for x in xs:
         wl.x.copy_(x)
-        _call(wl, ws, y)
+        _call(wl, ws, y, mode=mode)
         torch.cuda.synchronize()
         want.append(y.clone())
     wl.x.copy_(xs[0])
@@ -88,7 +95,7 @@ def test_layer_in_a_captured_graph(name):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        _call(wl, ws, y)
+        _call(wl, ws, y, mode=mode)
     torch.cuda.synchronize()
     junk = torch.randn(512, 512, device="cuda")
     for rep in range(2):
