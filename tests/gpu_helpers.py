@@ -29,9 +29,13 @@ TOL = {"f32": 1e-4, "bf16": 1e-2, "fp8": 3e-2}
 # when its largest element crosses a power of two).  Those few outputs move by
 # about one fp8 step: the largest deviation is held to the fp8 bar
 # (TOL["fp8"]).  Everything else is rounding of bf16 intermediates, so the
-# mean deviation over the tensor is held to TOL_MATCHED_MEAN (of max|ref|),
-# which a systematic loss of accuracy in the kernels would exceed.
-TOL_MATCHED_MEAN = 8e-4
+# 99th percentile and the mean of the deviation over the tensor are held to
+# TOL_MATCHED_P99 and TOL_MATCHED_MEAN (of max|ref|), which a systematic loss
+# of accuracy in the kernels would exceed (measured over every matched test,
+# W8A8, sub-channel W8A8 and W4A8, small and full size: max 2.3e-2, p99 at most
+# 2.9e-3, mean at most 4.0e-4).
+TOL_MATCHED_P99 = 5e-3
+TOL_MATCHED_MEAN = 6e-4
 
 
 def err_profile(got: np.ndarray, ref: np.ndarray) -> dict:
@@ -45,6 +49,7 @@ def check_matched(got: np.ndarray, ref: np.ndarray, what: str) -> dict:
     e = err_profile(got, ref)
     print(f"[matched] {what}: max {e['max']:.3e} p99 {e['p99']:.3e} mean {e['mean']:.3e}", flush=True)
     assert e["max"] <= TOL["fp8"], e
+    assert e["p99"] <= TOL_MATCHED_P99, e
     assert e["mean"] <= TOL_MATCHED_MEAN, e
     return e
 
@@ -163,6 +168,6 @@ def oracle_routing_from_logits(logits_ref, k, E):
 
 
 __all__ = ["TOL", "tol_for", "problem", "to_device", "f64", "run_layer", "oracle_layer",
-           "tile_edge_tokens", "oracle_inputs", "TOL_MATCHED_MEAN", "err_profile",
+           "tile_edge_tokens", "oracle_inputs", "TOL_MATCHED_MEAN", "TOL_MATCHED_P99", "err_profile",
            "check_matched", "PrefetchExperts", "oracle_routing_from_logits", "rel_err",
            "experts_from_bits", "shared_from_bits"]
