@@ -221,9 +221,11 @@ int stream_max_mt(int a_dtype);              // largest mt the stream kernel run
 // shapes (rows x weight rows): TILED_TALL 256 x 256 (expert FFNs), TILED_WIDE
 // 128 x 512 and TILED_NARROW 128 x 256 (two blocks per CU), TILED_SMALL
 // 32 x 128 (two blocks per CU; decode-sized groups), TILED_SMALLQ 64 x 256
-// (two blocks per CU; decode-sized groups with fp8 or MXFP8 activations).
-// Every set's bm must be tiled_bm(shape).
-enum : int { TILED_TALL = 0, TILED_WIDE = 1, TILED_NARROW = 2, TILED_SMALL = 3, TILED_SMALLQ = 4 };
+// (two blocks per CU; decode-sized groups with fp8 or MXFP8 activations),
+// TILED_SMALLD 32 x 64 (the ungated bf16-weight product of decode-sized
+// groups: the down projection).  Every set's bm must be tiled_bm(shape).
+enum : int { TILED_TALL = 0, TILED_WIDE = 1, TILED_NARROW = 2, TILED_SMALL = 3, TILED_SMALLQ = 4,
+             TILED_SMALLD = 5 };
 // a_dtype DT_FP8 (fp8 activations with fp8 weights, bf16 output, one block
 // per CU shapes only) needs every set's a_scale; DT_FP8S (the same with
 // sub-channel scales, K a multiple of kSubChannel, no K slices) every set's
