@@ -115,13 +115,18 @@ def test_layer_is_deterministic():
 
 @pytest.mark.parametrize("over", [dict(T=1), dict(T=3, E=64), dict(E=8, k=8), dict(T=257),
                                   dict(T=513, k=1),
-                                  # I = 128: the 32-row tiled shape (decode plans), with the
-                                  # one-launch permutation at 4, 8 and 16 mask words
+                                  # I = I_shared = 128 (K a multiple of the 128-deep stage):
+                                  # the 32-row tiled shape of decode plans, its down
+                                  # projection on 64-wide blocks, with the one-launch
+                                  # permutation at 4, 8 and 16 mask words
                                   dict(T=1, I=128), dict(T=300, E=64, k=6, I=128),
-                                  dict(T=700, E=32, k=2, I=128), dict(T=1000, E=256, k=8, I=128)])
+                                  dict(T=700, E=32, k=2, I=128), dict(T=1000, E=256, k=8, I=128),
+                                  # I = 2048: the down projection's 256-deep stages
+                                  dict(T=40, E=16, k=4, I=2048)])
 def test_layer_edge_shapes(over):
+    I = over.get("I", 64)
     cfg = shrink(CONFIGS["qwen_decode"], D=128, E=over.get("E", 16), k=over.get("k", 4),
-                 I=over.get("I", 64), I_shared=64, T=over["T"] if "T" in over else 40)
+                 I=I, I_shared=I if I >= 128 else 64, T=over["T"] if "T" in over else 40)
     wl = to_device(generate(cfg, seed=4))
     ref = oracle_layer(wl)
     res = run_layer(wl, logits_in=torch.from_numpy(ref["logits"]).cuda())
@@ -160,6 +165,32 @@ def test_device_router_expert_count_not_multiple_of_four(E):
     same = np.all(np.sort(idx.cpu().numpy(), 1) == np.sort(ref["idx"], 1), axis=1)
     assert same.mean() >= 0.99
     res = run_layer(wl)
+    same = np.all(np.sort(res["topk_idx"].cpu().numpy(), 1) == np.sort(ref["idx"], 1), axis=1)
+    assert same.mean() >= 0.99
+    assert rel_err(f64(res["y"])[same], ref["y"][same]) <= tol_for(cfg)
+
+
+# The router on 256-row tiles (from 4096 tokens with E a multiple of 256): a
+# ragged last M-tile (T = 4099) and two or four K slices of partial sums.
+@pytest.mark.parametrize("D,E", [(512, 512), (1024, 256)])
+def test_device_router_tall_tiles(D, E):
+    cfg = shrink(CONFIGS["qwen_prefill"], T=4099, D=D, E=E, k=4, I=64, I_shared=0, zipf=False)
+    print(f"[router 256-row tiles] T={cfg.T} D={D} E={E}", flush=True)
+    wl = to_device(generate(cfg, seed=13))
+    ref = oracle_layer(wl)
+    p = problem(cfg)
+    logits = torch.empty((cfg.T, E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda")
+    B.moe_route(p, wl.x, wl.wr, logits, False, idx, w)
+    torch.cuda.synchronize()
+    lr = ref["logits"].astype(np.float64)
+    assert np.max(np.abs(f64(logits) - lr)) <= 1e-5 * max(1.0, float(np.max(np.abs(lr))))
+    same = np.all(np.sort(idx.cpu().numpy(), 1) == np.sort(ref["idx"], 1), axis=1)
+    assert same.mean() >= 0.99
+    res = run_layer(wl)
+    # the layer adds the K slices' partial sums (moe_route writes whole sums)
+    assert np.max(np.abs(f64(res["logits"]) - lr)) <= 1e-5 * max(1.0, float(np.max(np.abs(lr))))
     same = np.all(np.sort(res["topk_idx"].cpu().numpy(), 1) == np.sort(ref["idx"], 1), axis=1)
     assert same.mean() >= 0.99
     assert rel_err(f64(res["y"])[same], ref["y"][same]) <= tol_for(cfg)
