@@ -383,6 +383,35 @@ moe_status_t moe_quantize_subchannel(const void* a, int32_t rows, int32_t cols, 
 moe_status_t moe_quantize_rows_mx(const void* a, int32_t rows, int32_t cols, int64_t lda, uint8_t* q,
                                   uint8_t* scale, void* stream);
 
+/*
+ * The kernel shape each product of moe_layer takes for a problem: the planning
+ * moe_layer itself runs, on the host only (no device call; callable without a
+ * GPU).  For tests and tools that need to know which path a problem covers.
+ *   router / gate_up / down   a moe_plan_shape_t (the router is planned even
+ *                             when the caller passes logits in);
+ *   router_slices             K slices of the router product, whose fp32
+ *                             partial sums the top-k step adds in slice order;
+ *   one_launch_permute        1 when the permutation and the M-tile table run
+ *                             as one launch, else 0.
+ * Returns the status moe_layer_workspace_size returns for p, or MOE_ERR_NULL
+ * for a null out.
+ */
+typedef enum {
+  MOE_PLAN_STREAM_16 = 0,       /* register-streamed GEMM, 16-row tiles */
+  MOE_PLAN_STREAM_32 = 1,       /* ... 32-row tiles */
+  MOE_PLAN_STREAM_64 = 2,       /* ... 64-row tiles */
+  MOE_PLAN_TILED_256x256 = 3,   /* LDS-tiled GEMM, rows x weight rows per block */
+  MOE_PLAN_TILED_128x512 = 4,
+  MOE_PLAN_TILED_128x256 = 5,
+  MOE_PLAN_TILED_32x128 = 6,
+  MOE_PLAN_TILED_64x256 = 7,
+  MOE_PLAN_TILED_32x64 = 8
+} moe_plan_shape_t;
+typedef struct moe_plan {
+  int32_t router, router_slices, gate_up, down, one_launch_permute;
+} moe_plan_t;
+moe_status_t moe_layer_plan(const moe_problem_t* p, moe_plan_t* out);
+
 /* Human-readable name of a status code (static string; "unknown status" for
  * any other value). */
 const char* moe_status_string(moe_status_t status);

@@ -28,6 +28,9 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3FN, "mxfp4": MOE_
 ACTS = {"silu": MOE_ACT_SILU, "gelu_tanh": MOE_ACT_GELU_TANH}
 POLICIES = {"auto": MOE_TILE_AUTO, "stream": MOE_TILE_STREAM, "lds": MOE_TILE_LDS}
 COMBINES = {"auto": MOE_COMBINE_AUTO, "separate": MOE_COMBINE_SEPARATE, "fused": MOE_COMBINE_FUSED}
+# moe_plan_shape_t codes, by name
+PLAN_SHAPES = ("stream16", "stream32", "stream64", "tiled256x256", "tiled128x512", "tiled128x256",
+               "tiled32x128", "tiled64x256", "tiled32x64")
 
 
 class MoeLibraryMissing(RuntimeError):
@@ -49,6 +52,11 @@ class MoeProblem(ctypes.Structure):
 _vp = ctypes.c_void_p
 
 
+class MoePlan(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("router", "router_slices", "gate_up", "down",
+                                              "one_launch_permute")]
+
+
 class MoeLayerArgs(ctypes.Structure):
     _fields_ = [(n, _vp) for n in (
         "x", "w_router", "logits_in", "w13", "s13", "w2", "s2", "w13_shared", "s13_shared",
@@ -68,6 +76,7 @@ _SIG = {
                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp],
     "moe_combine": [ctypes.POINTER(MoeProblem), _vp, _vp, _vp, _vp, _vp, _vp],
     "moe_layer_workspace_size": [ctypes.POINTER(MoeProblem), ctypes.POINTER(ctypes.c_size_t)],
+    "moe_layer_plan": [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoePlan)],
     "moe_layer": [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeLayerArgs), _vp, ctypes.c_size_t, _vp],
     "moe_layer_noalloc_max_bytes": [],
     "moe_layer_noalloc": [ctypes.POINTER(MoeProblem), ctypes.POINTER(MoeLayerArgs), _vp],
@@ -185,6 +194,17 @@ def moe_layer_workspace_size(p: MoeProblem) -> int:
     n = ctypes.c_size_t(0)
     _check(lib().moe_layer_workspace_size(ctypes.byref(p), ctypes.byref(n)), "moe_layer_workspace_size")
     return n.value
+
+
+def moe_layer_plan(p: MoeProblem) -> dict:
+    """The kernel shape of each product moe_layer runs for p (host planning
+    only): router / gate_up / down by name (PLAN_SHAPES), the router's K
+    slices, and whether the permutation is one launch."""
+    out = MoePlan()
+    _check(lib().moe_layer_plan(ctypes.byref(p), ctypes.byref(out)), "moe_layer_plan")
+    return {"router": PLAN_SHAPES[out.router], "router_slices": out.router_slices,
+            "gate_up": PLAN_SHAPES[out.gate_up], "down": PLAN_SHAPES[out.down],
+            "one_launch_permute": bool(out.one_launch_permute)}
 
 
 def layer_args(**kw) -> MoeLayerArgs:

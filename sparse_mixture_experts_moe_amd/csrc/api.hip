@@ -726,6 +726,44 @@ moe_status_t moe_layer_workspace_size(const moe_problem_t* p, size_t* bytes) {
   return MOE_OK;
 }
 
+moe_status_t moe_layer_plan(const moe_problem_t* p, moe_plan_t* out) {
+  moe_status_t st = check_problem(p, true, true);
+  if (st != MOE_OK) return st;
+  if (!out) return MOE_ERR_NULL;
+  const LayerLayout L = layer_layout(p);
+  // a plan's shape as the launch resolves it: the dense 128-row tiles take the
+  // wide or the narrow block per launch (the sets it covers, as moe_layer
+  // groups them: one launch per weight dtype)
+  const bool split_sets = p->w_dtype != p->shared_w_dtype && p->I_shared;
+  auto code = [&](const Plan& pl, bool gated, int n_shared, int n_routed) -> int32_t {
+    if (!pl.tiled) return pl.mt == 1 ? MOE_PLAN_STREAM_16 : pl.mt == 2 ? MOE_PLAN_STREAM_32 : MOE_PLAN_STREAM_64;
+    int shape = pl.shape;
+    if (shape < 0) {
+      GArgs g{};
+      if (n_shared > 0 && !split_sets) g.s[g.nsets++].n_out = n_shared;
+      g.s[g.nsets++].n_out = n_routed;
+      shape = pick_dense_shape(g, gated);
+    }
+    switch (shape) {
+      case TILED_TALL: return MOE_PLAN_TILED_256x256;
+      case TILED_WIDE: return MOE_PLAN_TILED_128x512;
+      case TILED_NARROW: return MOE_PLAN_TILED_128x256;
+      case TILED_SMALL: return MOE_PLAN_TILED_32x128;
+      case TILED_SMALLQ: return MOE_PLAN_TILED_64x256;
+      case TILED_SMALLD:
+      default: return MOE_PLAN_TILED_32x64;
+    }
+  };
+  const Plan rp = router_plan(p);
+  out->router = code(rp, false, 0, p->E);
+  out->router_slices = L.splits;
+  out->gate_up = code(L.plan, true, p->I_shared, p->I);
+  out->down = code(L.plan2, false, p->I_shared ? p->D : 0, p->D);
+  out->one_launch_permute = p->T <= perm_small_max_tokens() &&
+                            (!L.plan.tiled || L.plan.shape == TILED_SMALL || L.plan.shape == TILED_SMALLQ);
+  return MOE_OK;
+}
+
 moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* ws, size_t ws_bytes,
                        void* stream) {
   moe_status_t st = check_layer_args(p, A);

@@ -12,6 +12,8 @@
  *  - moe_layer and moe_layer_noalloc with a missing pointer return
  *    MOE_ERR_NULL for accepted problems and the same code as
  *    moe_layer_workspace_size otherwise;
+ *  - moe_layer_plan answers as moe_layer_workspace_size does, with shape
+ *    codes of moe_plan_shape_t and 1..D/64 router K slices;
  *  - status strings and stage names exist for every value, in range or not.
  * Prints "ok" and exits 0 when every check passes.
  */
@@ -129,6 +131,20 @@ int main(void) {
     CHECK(sl == (st == MOE_OK ? MOE_ERR_NULL : st), "moe_layer %d vs workspace %d", (int)sl, (int)st);
     moe_status_t sn = moe_layer_noalloc(&p, NULL, NULL);
     CHECK(sn == (st == MOE_OK ? MOE_ERR_NULL : st), "noalloc %d vs workspace %d", (int)sn, (int)st);
+    /* the plan: the same answer as the workspace, codes in range */
+    moe_plan_t plan;
+    memset(&plan, 0xff, sizeof plan);
+    moe_status_t sq = moe_layer_plan(&p, &plan);
+    CHECK(sq == st, "plan %d vs workspace %d", (int)sq, (int)st);
+    CHECK(moe_layer_plan(&p, NULL) == (st == MOE_OK ? MOE_ERR_NULL : st), "plan with null out");
+    if (sq == MOE_OK) {
+      CHECK(plan.router >= MOE_PLAN_STREAM_16 && plan.router <= MOE_PLAN_TILED_32x64 &&
+                plan.gate_up >= MOE_PLAN_STREAM_16 && plan.gate_up <= MOE_PLAN_TILED_32x64 &&
+                plan.down >= MOE_PLAN_STREAM_16 && plan.down <= MOE_PLAN_TILED_32x64,
+            "plan codes %d %d %d", (int)plan.router, (int)plan.gate_up, (int)plan.down);
+      CHECK(plan.router_slices >= 1 && plan.router_slices <= p.D / 64, "router slices %d", (int)plan.router_slices);
+      CHECK(plan.one_launch_permute == 0 || plan.one_launch_permute == 1, "permute flag");
+    }
 
     size_t pws = 0;
     moe_status_t sp = moe_permute_workspace_size(&p, &pws);

@@ -113,20 +113,25 @@ def test_layer_is_deterministic():
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
-@pytest.mark.parametrize("over", [dict(T=1), dict(T=3, E=64), dict(E=8, k=8), dict(T=257),
-                                  dict(T=513, k=1),
-                                  # I = I_shared = 128 (K a multiple of the 128-deep stage):
-                                  # the 32-row tiled shape of decode plans, its down
-                                  # projection on 64-wide blocks, with the one-launch
-                                  # permutation at 4, 8 and 16 mask words
-                                  dict(T=1, I=128), dict(T=300, E=64, k=6, I=128),
-                                  dict(T=700, E=32, k=2, I=128), dict(T=1000, E=256, k=8, I=128),
-                                  # I = 2048: the down projection's 256-deep stages
-                                  dict(T=40, E=16, k=4, I=2048)])
-def test_layer_edge_shapes(over):
+EDGE = [dict(T=1), dict(T=3, E=64), dict(E=8, k=8), dict(T=257), dict(T=513, k=1),
+        # I = I_shared = 128 (K a multiple of the 128-deep stage): the 32-row
+        # tiled shape of decode plans, its down projection on 64-wide blocks,
+        # with the one-launch permutation at 4, 8 and 16 mask words
+        dict(T=1, I=128), dict(T=300, E=64, k=6, I=128), dict(T=700, E=32, k=2, I=128),
+        dict(T=1000, E=256, k=8, I=128),
+        # I = 2048: the down projection's 256-deep stages
+        dict(T=40, E=16, k=4, I=2048)]
+
+
+def edge_config(over):
     I = over.get("I", 64)
-    cfg = shrink(CONFIGS["qwen_decode"], D=128, E=over.get("E", 16), k=over.get("k", 4),
-                 I=I, I_shared=I if I >= 128 else 64, T=over["T"] if "T" in over else 40)
+    return shrink(CONFIGS["qwen_decode"], D=128, E=over.get("E", 16), k=over.get("k", 4),
+                  I=I, I_shared=I if I >= 128 else 64, T=over["T"] if "T" in over else 40)
+
+
+@pytest.mark.parametrize("over", EDGE)
+def test_layer_edge_shapes(over):
+    cfg = edge_config(over)
     wl = to_device(generate(cfg, seed=4))
     ref = oracle_layer(wl)
     res = run_layer(wl, logits_in=torch.from_numpy(ref["logits"]).cuda())
@@ -172,9 +177,16 @@ def test_device_router_expert_count_not_multiple_of_four(E):
 
 # The router on 256-row tiles (from 4096 tokens with E a multiple of 256): a
 # ragged last M-tile (T = 4099) and two or four K slices of partial sums.
-@pytest.mark.parametrize("D,E", [(512, 512), (1024, 256)])
+ROUTER_TALL = [(512, 512), (1024, 256)]
+
+
+def router_tall_config(D, E):
+    return shrink(CONFIGS["qwen_prefill"], T=4099, D=D, E=E, k=4, I=64, I_shared=0, zipf=False)
+
+
+@pytest.mark.parametrize("D,E", ROUTER_TALL)
 def test_device_router_tall_tiles(D, E):
-    cfg = shrink(CONFIGS["qwen_prefill"], T=4099, D=D, E=E, k=4, I=64, I_shared=0, zipf=False)
+    cfg = router_tall_config(D, E)
     print(f"[router 256-row tiles] T={cfg.T} D={D} E={E}", flush=True)
     wl = to_device(generate(cfg, seed=13))
     ref = oracle_layer(wl)
