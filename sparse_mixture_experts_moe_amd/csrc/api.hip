@@ -206,16 +206,17 @@ Plan make_plan(const moe_problem_t* p, double mean_rows) {
 }
 
 // Down projection of the fused layer.  Where gate/up runs on 256-row tiles
-// (bf16, up to kTallMean rows per expert) and D fills 512-wide blocks, the
-// down projection takes 128 x 512 tiles from a tile table of its own: its K is
-// I rather than D, so a 256-row tile's blocks are short, and 128-row blocks
-// measured faster there (Qwen prefill down projection 1.74 -> 1.64 ms) while
-// gate/up keeps the 256-row tiles.
+// (bf16, up to kTallMean rows per expert), the down projection takes 128-row
+// tiles from a tile table of its own (128 x 512 blocks, or 128 x 256 where
+// those pad D less): its K is I rather than D, so a 256-row tile's blocks are
+// short, and 128-row blocks measured faster there (Qwen prefill down
+// projection 1.74 -> 1.64 ms; Gemma, D = 2816 on 128 x 256 blocks, 0.211 ->
+// 0.202 ms) while gate/up keeps the 256-row tiles.
 // Under the 32-row decode tiles with bf16 weights, the down projection takes
 // 64-wide weight blocks on the same M-tile table (twice the blocks; Qwen decode
 // down projection 0.501 -> 0.487 ms).
 Plan down_plan(const moe_problem_t* p, const Plan& up) {
-  if (up.tiled && up.shape == TILED_TALL && !quantised(p) && p->D % 512 == 0)
+  if (up.tiled && up.shape == TILED_TALL && !quantised(p))
     return Plan{true, 0, tiled_bm(TILED_WIDE), -1};
   if (up.tiled && up.shape == TILED_SMALL && p->w_dtype == MOE_BF16 &&
       (!p->I_shared || p->shared_w_dtype == MOE_BF16))

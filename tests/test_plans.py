@@ -28,7 +28,7 @@ def plan(cfg, policy="auto", act_quant=0):
 FULL = {
     ("qwen_decode", 0): ("stream64", 16, "tiled32x128", "tiled32x64", True),
     ("qwen_prefill", 0): ("tiled256x256", 4, "tiled256x256", "tiled128x512", False),
-    ("gemma", 0): ("tiled128x256", 11, "tiled256x256", "tiled256x256", False),
+    ("gemma", 0): ("tiled128x256", 11, "tiled256x256", "tiled128x256", False),
     ("ling_prefill", 0): ("tiled256x256", 4, "tiled128x512", "tiled128x512", False),
     ("ling_decode", 0): ("tiled128x256", 32, "tiled32x128", "tiled32x128", True),
     ("ling_prefill", B.MOE_ACT_QUANT_FP8_ROW): ("tiled256x256", 4, "tiled128x512", "tiled128x512", False),
