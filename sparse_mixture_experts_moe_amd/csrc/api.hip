@@ -382,8 +382,15 @@ struct Carve {
 };
 
 // Arrival counters of the fused combine: one per token and N block of the
-// down projection, sized for the narrowest tiled block (128 output columns).
-int64_t fused_max_nb(const moe_problem_t* p) { return (p->D + 63) / 64; }   // 64-wide blocks at the least
+// down projection, sized for the narrowest tiled block (64 output columns).
+int64_t fused_max_nb(const moe_problem_t* p) { return (p->D + 63) / 64; }
+
+// The permutation and the M-tile table run as one single-block launch for
+// small batches under the decode-sized (or streamed) plans.
+bool one_launch_permute(const moe_problem_t* p, const Plan& pl) {
+  return p->T <= perm_small_max_tokens() &&
+         (!pl.tiled || pl.shape == TILED_SMALL || pl.shape == TILED_SMALLQ);
+}
 
 struct LayerLayout {
   size_t logits, idx, w, counts, offsets, row_token, row_of_slot, blk, rank, tiles, ntiles;
@@ -760,8 +767,7 @@ moe_status_t moe_layer_plan(const moe_problem_t* p, moe_plan_t* out) {
   out->router_slices = L.splits;
   out->gate_up = code(L.plan, true, p->I_shared, p->I);
   out->down = code(L.plan2, false, p->I_shared ? p->D : 0, p->D);
-  out->one_launch_permute = p->T <= perm_small_max_tokens() &&
-                            (!L.plan.tiled || L.plan.shape == TILED_SMALL || L.plan.shape == TILED_SMALLQ);
+  out->one_launch_permute = one_launch_permute(p, L.plan);
   return MOE_OK;
 }
 
@@ -814,8 +820,7 @@ moe_status_t moe_layer(const moe_problem_t* p, const moe_layer_args_t* A, void* 
                                    idx, tw, s));
   }
   // 2. permutation and the M-tile table (one launch for small batches)
-  if (p->T <= perm_small_max_tokens() &&
-      (!pl.tiled || pl.shape == TILED_SMALL || pl.shape == TILED_SMALLQ)) {
+  if (one_launch_permute(p, pl)) {
     StageScope sc(ST_PERMUTE, s);
     MOE_LAUNCH(launch_permute_small(idx, p->T, p->k, p->E, counts, offsets, row_token, row_of_slot,
                                     pl.bm, L.tile_ub, pl.tiled, tiles, ntiles, s));
