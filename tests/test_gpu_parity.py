@@ -263,6 +263,31 @@ def test_moe_route_plain_softmax(T, E, k):
     assert np.allclose(w.cpu().numpy(), rw, rtol=PLAIN_W_RTOL, atol=0)
 
 
+@pytest.mark.parametrize("name,logits_given", [("qwen_decode_like", False), ("qwen_zipf", False),
+                                                ("qwen_ragged", True), ("ling_fp8", False)])
+def test_plan_query_matches_the_stages_run(name, logits_given):
+    """moe_layer_plan describes what moe_layer runs: the stage record shows
+    the tile-table stage exactly when the plan says the permutation is not one
+    launch, and the router stage exactly when logits are not passed in."""
+    cfg = SMALL[name]
+    plan = B.moe_layer_plan(problem(cfg))
+    wl = to_device(generate(cfg, seed=21))
+    logits_in = None
+    if logits_given:
+        logits_in = torch.from_numpy(oracle_layer(wl)["logits"]).cuda()
+    B.moe_timing_read()
+    B.moe_timing_enable(True)
+    try:
+        run_layer(wl, logits_in=logits_in, want=())
+        torch.cuda.synchronize()
+    finally:
+        B.moe_timing_enable(False)
+    rec = B.moe_timing_read()
+    assert rec["permute"][1] == 1 and rec["topk_softmax"][1] == 1
+    assert rec["tile_table"][1] == (0 if plan["one_launch_permute"] else 1), (name, plan)
+    assert rec["router_gemm"][1] == (0 if logits_given else 1), name
+
+
 def test_stage_timing_mask():
     """Timing restricted to one stage records that stage only, and the output
     is the same as with timing off."""
