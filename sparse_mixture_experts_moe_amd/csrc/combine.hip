@@ -20,7 +20,11 @@ constexpr int CHUNK = THREADS * 8;   // hidden elements per block
 constexpr int MAXK = 32;
 
 // 8 elements as stored (bf16: 16 bytes; fp32: 32 bytes), loaded without use
-// so that several rows' loads can be in flight together
+// so that several rows' loads can be in flight together.  bf16 rows are read
+// with the non-temporal hint: every expert row is read exactly once (Ling
+// prefill combine 0.519 -> 0.462 ms; the next layer's router, reading x right
+// after, 107 -> 122 us; layer 14.33 -> 14.25 ms).
+typedef unsigned u32x4v __attribute__((ext_vector_type(4)));
 template <int DT> struct Raw8;
 template <> struct Raw8<DT_BF16> { uint4 q; };
 template <> struct Raw8<DT_F32> { float4 a, b; };
@@ -29,7 +33,9 @@ template <int DT>
 __device__ __forceinline__ Raw8<DT> load_raw(const void* base, int64_t off) {
   Raw8<DT> r;
   if constexpr (DT == DT_BF16) {
-    r.q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    const u32x4v v =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(static_cast<const uint16_t*>(base) + off));
+    r.q = uint4{v[0], v[1], v[2], v[3]};
   } else {
     const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
     r.a = p[0];
