@@ -45,6 +45,18 @@ def test_quantize_rows_bit_exact(rows, cols, lda):
         mids = (TABLE[codes] + TABLE[codes + 1]) / 2
         mids[0] = 448.0
         a[3, :cols] = (mids * 2.0 ** -5).astype(np.float32)
+    if rows > 6:
+        # exact midpoints again, reached through scales 3, 5 and 7 (the row
+        # maximum 448 s): the quotients x / s are ties that a product with
+        # the rounded reciprocal of s misses by an ulp
+        for rr, m in ((4, 3.0), (5, 5.0), (6, 7.0)):
+            codes = rng.integers(0, 0x7E, size=cols)
+            row = ((TABLE[codes] + TABLE[codes + 1]) / 2 * m).astype(np.float32)
+            row *= rng.choice([-1.0, 1.0], size=cols).astype(np.float32)
+            row[0] = 448.0 * m
+            keep = torch.from_numpy(row).to(torch.bfloat16).float().numpy() == row
+            a[rr, :cols] = np.where(keep, row, 0.0)
+            assert keep.mean() > 0.9
     at = torch.from_numpy(a).to(torch.bfloat16).cuda()
     q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
     s = torch.empty(rows, dtype=torch.float32, device="cuda")

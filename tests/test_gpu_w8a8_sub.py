@@ -51,6 +51,18 @@ def test_quantize_subchannel_bit_exact(rows, cols, lda):
         mids = (TABLE[codes] + TABLE[codes + 1]) / 2
         mids[0] = 448.0
         a[3, :W] = (mids * 2.0 ** -5).astype(np.float32)
+    if rows > 4:
+        # exact midpoints through the slice scales 3, 5 and 7 (slice maximum
+        # 448 s), one slice each: ties that a product with the rounded
+        # reciprocal of s misses by an ulp
+        for u, m in zip(range(cols // W), (3.0, 5.0, 7.0)):
+            codes = rng.integers(0, 0x7E, size=W)
+            sl = ((TABLE[codes] + TABLE[codes + 1]) / 2 * m).astype(np.float32)
+            sl *= rng.choice([-1.0, 1.0], size=W).astype(np.float32)
+            sl[0] = 448.0 * m
+            keep = torch.from_numpy(sl).to(torch.bfloat16).float().numpy() == sl
+            a[4, u * W:(u + 1) * W] = np.where(keep, sl, 0.0)
+            assert keep.mean() > 0.9
     at = torch.from_numpy(a).to(torch.bfloat16).cuda()
     q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
     s = torch.empty((cols // W, rows), dtype=torch.float32, device="cuda")
