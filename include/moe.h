@@ -465,6 +465,16 @@ moe_status_t moe_probe_mfma(int32_t dtype, const void* operands, int32_t iters, 
  */
 moe_status_t moe_debug_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int32_t n, void* stream);
 
+/*
+ * Diagnostic: encode n (even) fp32 values, each clamped to +-448 first, to
+ * fp8 e4m3fn codes (nearest representable value, ties to the even code) with
+ * the exact device routine the activation quantisers use, so the hardware
+ * conversion can be checked against the format definition.  v [n] float,
+ * out [n] uint8 (device pointers).  Non-finite inputs are outside the
+ * contract.
+ */
+moe_status_t moe_debug_f32_to_fp8(const float* v, uint8_t* out, int32_t n, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -86,6 +86,7 @@ _SIG = {
     "moe_stage_count": [],
     "moe_stage_name": [ctypes.c_int32],
     "moe_debug_fp8_to_bf16": [_vp, _vp, ctypes.c_int32, _vp],
+    "moe_debug_f32_to_fp8": [_vp, _vp, ctypes.c_int32, _vp],
     "moe_probe_hbm_read": [_vp, ctypes.c_int64, _vp, _vp],
     "moe_probe_mfma_sink_floats": [],
     "moe_probe_mfma": [ctypes.c_int32, _vp, ctypes.c_int32, _vp, ctypes.POINTER(ctypes.c_double), _vp],
@@ -292,6 +293,10 @@ def moe_probe_mfma(dtype: str, operands, iters: int, sink, stream=None) -> float
 
 def moe_debug_fp8_to_bf16(codes, out, n: int, stream=None):
     _check(lib().moe_debug_fp8_to_bf16(_p(codes), _p(out), n, _stream(stream)), "moe_debug_fp8_to_bf16")
+
+
+def moe_debug_f32_to_fp8(v, out, n: int, stream=None):
+    _check(lib().moe_debug_f32_to_fp8(_p(v), _p(out), n, _stream(stream)), "moe_debug_f32_to_fp8")
 
 
 _OUTS = {"logits_out": ("E", "f32"), "topk_idx_out": ("k", "i32"), "topk_w_out": ("k", "f32"),

@@ -30,31 +30,17 @@ namespace {
 constexpr int QMAX = 16384;           // widest row: 64 lanes x 32 chunks of 8
 static_assert(kSubChannel == 64 * 8, "a sub-channel slice is one chunk per lane");
 
-// e4m3fn code of v with |v| <= 448, from the format: sign, 4 exponent bits
-// (bias 7), 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9.
-// Round to nearest, ties to the even mantissa.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
-  const float a = fabsf(v);
-  uint32_t code;
-  if (a < 0.015625f) {
-    // below 2^-6 the grid step is 2^-9: rintf rounds a * 2^9 (exact) to
-    // nearest even; 8 is 2^-6, the first normal code
-    code = static_cast<uint32_t>(rintf(a * 512.0f));
-  } else {
-    const uint32_t ab = __float_as_uint(a);
-    uint32_t e = (ab >> 23) - 120u;          // fp32 exponent bias 127 -> 7
-    uint32_t m3 = (ab >> 20) & 7u;
-    const uint32_t rem = ab & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
-    if (m3 == 8u) {
-      m3 = 0;
-      ++e;
-    }
-    code = (e << 3) | m3;
-  }
-  return sign | code;
+// e4m3fn codes of a pair of values within +-448 (low byte: a), the nearest
+// representable value with ties to the even code: the hardware fp32 -> fp8
+// pair conversion, which on this target produces the e4m3fn format (bias 7,
+// subnormals m * 2^-9, no infinities).  Checked against the format's
+// definition by moe_debug_f32_to_fp8 (every fp32 value from 2^-20 to 448,
+// both signs, gave the same codes as a bit-level encoder of the format).
+__device__ __forceinline__ uint32_t e4m3_pair(float a, float b) {
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false)) & 0xFFFFu;
 }
+
+__device__ __forceinline__ float clamp448(float v) { return fminf(fmaxf(v, -448.0f), 448.0f); }
 
 // One wavefront per row, 4 rows per block: lane l holds the row's 16-byte
 // chunks l, l + 64, ... (NCH of them) in registers between the max and the
@@ -106,9 +92,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float x0 = __uint_as_float(w[j] << 16), x1 = __uint_as_float(w[j] & 0xFFFF0000u);
-      const float t0 = fminf(fmaxf(__fdiv_rn(x0, s), -448.0f), 448.0f);
-      const float t1 = fminf(fmaxf(__fdiv_rn(x1, s), -448.0f), 448.0f);
-      const uint32_t pair = e4m3_code(t0) | (e4m3_code(t1) << 8);
+      const uint32_t pair = e4m3_pair(clamp448(__fdiv_rn(x0, s)), clamp448(__fdiv_rn(x1, s)));
       packed[j >> 1] |= pair << (16 * (j & 1));
     }
     *reinterpret_cast<uint2*>(qrow + 8 * c) = uint2{packed[0], packed[1]};
@@ -162,8 +146,7 @@ __global__ __launch_bounds__(256) void quant_rows_mx_kernel(const uint16_t* __re
     for (int j = 0; j < 4; ++j) {
       const float x0 = ldexpf(__uint_as_float(w[j] << 16), -ex);
       const float x1 = ldexpf(__uint_as_float(w[j] & 0xFFFF0000u), -ex);
-      const uint32_t pair = e4m3_code(fminf(fmaxf(x0, -448.0f), 448.0f)) |
-                            (e4m3_code(fminf(fmaxf(x1, -448.0f), 448.0f)) << 8);
+      const uint32_t pair = e4m3_pair(clamp448(x0), clamp448(x1));
       packed[j >> 1] |= pair << (16 * (j & 1));
     }
     *reinterpret_cast<uint2*>(qrow + 8 * c) = uint2{packed[0], packed[1]};
@@ -188,9 +171,28 @@ hipError_t go(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q, fl
   return hipGetLastError();
 }
 
+// e4m3fn codes of v[0..n) (n even), each clamped to +-448 first, with the
+// quantisers' encoder.
+__global__ __launch_bounds__(256) void fp8_encode_kernel(const float* __restrict__ v, uint8_t* __restrict__ out,
+                                                         int64_t pairs) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= pairs) return;
+  const uint32_t p = e4m3_pair(clamp448(v[2 * i]), clamp448(v[2 * i + 1]));
+  out[2 * i] = static_cast<uint8_t>(p & 0xFFu);
+  out[2 * i + 1] = static_cast<uint8_t>(p >> 8);
+}
+
 }  // namespace
 
 int quant_max_cols() { return QMAX; }
+
+hipError_t launch_fp8_encode(const float* v, uint8_t* out, int n, hipStream_t s) {
+  if (n < 0 || n % 2) return hipErrorInvalidValue;
+  const int64_t pairs = n / 2;
+  if (pairs == 0) return hipSuccess;
+  fp8_encode_kernel<<<static_cast<unsigned>((pairs + 255) / 256), 256, 0, s>>>(v, out, pairs);
+  return hipGetLastError();
+}
 
 hipError_t launch_quant_rows(const uint16_t* a, int rows, int cols, int64_t lda, uint8_t* q,
                              float* scale, hipStream_t s) {

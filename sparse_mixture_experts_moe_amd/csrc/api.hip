@@ -1158,4 +1158,11 @@ moe_status_t moe_debug_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int32_t 
   return MOE_OK;
 }
 
+moe_status_t moe_debug_f32_to_fp8(const float* v, uint8_t* out, int32_t n, void* stream) {
+  if (!v || !out) return MOE_ERR_NULL;
+  if (n < 0 || n % 2) return MOE_ERR_SHAPE;
+  MOE_LAUNCH(launch_fp8_encode(v, out, n, static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
 }  // extern "C"

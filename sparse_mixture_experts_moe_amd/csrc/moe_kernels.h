@@ -263,6 +263,7 @@ hipError_t launch_quant_rows_mx(const uint16_t* a, int rows, int cols, int64_t l
 
 // Decode n (multiple of 8) fp8 e4m3fn codes to bf16 with the GEMM's own decoder.
 hipError_t launch_fp8_decode(const uint8_t* codes, uint16_t* out, int n, hipStream_t s);
+hipError_t launch_fp8_encode(const float* v, uint8_t* out, int n, hipStream_t s);
 
 // Measurement probes: a streaming read of `bytes` (a multiple of 16) with
 // eight 16-byte loads in flight per thread (sink: 1024 words, written only on

@@ -257,6 +257,8 @@ def test_null_and_workspace_errors(lib):
     assert lib.moe_grouped_ffn(ctypes.byref(p), 0, 10, fake, None, fake, fake, None, fake, None,
                                fake, fake, fake, 1 << 20, None) == B.MOE_ERR_SHAPE
     assert lib.moe_debug_fp8_to_bf16(fake, fake, 7, None) == B.MOE_ERR_SHAPE
+    assert lib.moe_debug_f32_to_fp8(fake, fake, 7, None) == B.MOE_ERR_SHAPE
+    assert lib.moe_debug_f32_to_fp8(None, fake, 8, None) == B.MOE_ERR_NULL
 
 
 def test_grouped_ffn_rows_bound(lib):

@@ -5,6 +5,7 @@ import torch
 
 from gpu_helpers import (f64, oracle_inputs, oracle_layer, problem, rel_err, run_layer, to_device,
                          tol_for)
+from oracle.actquant import encode_e4m3fn
 from oracle.formats import fp8_e4m3fn_table
 from oracle.moe import layer, layer_tokens, permute, router_logits, topk_softmax
 from sparse_mixture_experts_moe_amd import binding as B
@@ -70,6 +71,35 @@ def test_fp8_decode_all_256_codes():
     assert np.all(np.isnan(got[nan]))
     assert np.array_equal(got[~nan], ref[~nan])
     assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_fp8_encode_against_the_format():
+    """The activation quantisers' fp32 -> e4m3fn encoder against the oracle's
+    (nearest value, ties to the even code, saturating at 448): every code's
+    value and every midpoint between neighbouring codes with four fp32 ulps on
+    either side, 2^22 values spread over 2^-24 .. 2^10, values past 448, both
+    signs."""
+    pos = fp8_e4m3fn_table()[:0x7F].astype(np.float32)            # 0 .. 448
+    base = np.concatenate([pos, ((pos[:-1].astype(np.float64) + pos[1:]) / 2).astype(np.float32)])
+    vals, up, dn = [base], base.copy(), base.copy()
+    for _ in range(4):
+        up = np.nextafter(up, np.float32(np.inf))
+        dn = np.nextafter(dn, np.float32(-np.inf))
+        vals += [up, dn]
+    rng = np.random.default_rng(5)
+    n = 1 << 22
+    vals.append((rng.standard_normal(n) * np.exp2(rng.uniform(-24, 10, n))).astype(np.float32))
+    vals.append(np.array([448.0, 460.0, 480.0, 1.0e30, 2.0 ** -10, 2.0 ** -11], np.float32))
+    v = np.concatenate(vals)
+    v = np.concatenate([v, -v])
+    got = torch.empty(v.size, dtype=torch.uint8, device="cuda")
+    B.moe_debug_f32_to_fp8(torch.from_numpy(v).cuda(), got, v.size)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    ref = encode_e4m3fn(v)
+    same = (got == ref) | (((got & 0x7F) == 0) & ((ref & 0x7F) == 0))   # +0 and -0 alike
+    assert same.all(), [(float(x), hex(int(g)), hex(int(r))) for x, g, r in
+                        zip(v[~same][:8], got[~same][:8], ref[~same][:8])]
 
 
 # ------------------------------------------------------------------ whole layer, small
