@@ -131,17 +131,22 @@ __global__ __launch_bounds__(256) void topk_softmax_wave_kernel(
     const int e = lane + 64 * j;
     v[j] = e < E ? row[e] : -__builtin_inff();
   }
-  for (int s0 = 1; s0 < splits; ++s0) {
-    float pv[EPL];
+  // every slice's loads first, then the additions in slice order
+  float pv[kWaveSplits - 1][EPL];
+#pragma unroll
+  for (int s0 = 1; s0 < kWaveSplits; ++s0)
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + 64 * j;
-      pv[j] = e < E ? row[s0 * slice + e] : 0.f;
+      pv[s0 - 1][j] = (s0 < splits && e < E) ? row[s0 * slice + e] : 0.f;
     }
 #pragma unroll
-    for (int j = 0; j < EPL; ++j)
-      if (lane + 64 * j < E) v[j] += pv[j];
-  }
+  for (int s0 = 1; s0 < kWaveSplits; ++s0)
+    if (s0 < splits) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        if (lane + 64 * j < E) v[j] += pv[s0 - 1][j];
+    }
   if (logits_out) {
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
